@@ -1,0 +1,272 @@
+"""Python binding of libmuon, the MI355X batched Muon step (C ABI in
+include/muon.h).
+
+This module only marshals arguments: it turns torch tensors into device
+pointers and shapes, passes the current HIP stream, and maps status codes
+to exceptions. Every step of the computation runs in the library's HIP
+kernels; there is no fallback. If libmuon.so is missing, importing the
+library raises.
+
+A 3-D tensor [E, M, N] is passed as E separate M x N matrices (the
+HyperParallel-FSDP paper, arXiv:2609.21594 section 6.3: an expert weight
+holds E independent matrices and is never flattened).
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Iterable, List, Optional, Sequence, Tuple
+
+import torch  # loaded first: libmuon then binds to torch's HIP runtime
+
+__all__ = ["MuonError", "muon_group_step", "muon_step", "muon_orthogonalize", "plan_query",
+           "profile_enable", "profile_read", "version", "library_path", "load"]
+
+MUON_F32, MUON_BF16 = 0, 1
+_DTYPES = {torch.float32: MUON_F32, torch.bfloat16: MUON_BF16}
+_STATUS = {0: "ok", 1: "invalid argument", 2: "unsupported", 3: "misaligned pointer",
+           4: "out of memory", 5: "HIP error"}
+
+
+class MuonError(RuntimeError):
+    def __init__(self, status: int, message: str):
+        super().__init__(f"{_STATUS.get(status, status)}: {message}")
+        self.status = status
+
+
+class Options(ctypes.Structure):
+    _fields_ = [("nesterov", ctypes.c_int), ("momentum_form", ctypes.c_int),
+                ("weight_decay", ctypes.c_float), ("scale_rule", ctypes.c_int),
+                ("rms_target", ctypes.c_float), ("eps", ctypes.c_float),
+                ("coeffs", ctypes.POINTER(ctypes.c_float)), ("batch_cap_elems", ctypes.c_size_t)]
+
+
+class Matrix(ctypes.Structure):
+    _fields_ = [("param", ctypes.c_void_p), ("grad", ctypes.c_void_p), ("momentum", ctypes.c_void_p),
+                ("rows", ctypes.c_int), ("cols", ctypes.c_int)]
+
+
+class PlanBatch(ctypes.Structure):
+    _fields_ = [("group", ctypes.c_int), ("m", ctypes.c_int), ("n", ctypes.c_int),
+                ("m_pad", ctypes.c_int), ("n_pad", ctypes.c_int), ("first", ctypes.c_int),
+                ("count", ctypes.c_int)]
+
+
+class ProfileEntry(ctypes.Structure):
+    _fields_ = [("name", ctypes.c_char * 32), ("launches", ctypes.c_int), ("total_ms", ctypes.c_double),
+                ("flops", ctypes.c_double), ("bytes", ctypes.c_double)]
+
+
+_LIB = None
+SYMBOLS = ("muon_default_options", "muon_group_step", "muon_step", "muon_orthogonalize",
+           "muon_plan_query", "muon_status_string", "muon_last_error", "muon_version",
+           "muon_profile_enable", "muon_profile_read")
+
+
+def library_path() -> str:
+    return os.environ.get("MUON_LIBRARY", os.path.join(os.path.dirname(os.path.abspath(__file__)), "libmuon.so"))
+
+
+def load() -> ctypes.CDLL:
+    """Loads libmuon.so (raises ImportError if it is not built)."""
+    global _LIB
+    if _LIB is not None:
+        return _LIB
+    path = library_path()
+    if not os.path.exists(path):
+        raise ImportError(f"{path} is not built: run `python -m newton_schulz_10_amd.build`")
+    L = ctypes.CDLL(path)
+    vp, i, f = ctypes.c_void_p, ctypes.c_int, ctypes.c_float
+    L.muon_default_options.argtypes = [ctypes.POINTER(Options)]
+    L.muon_default_options.restype = None
+    L.muon_group_step.argtypes = [ctypes.POINTER(vp), ctypes.POINTER(vp), ctypes.POINTER(vp), i, i, i,
+                                  f, f, i, i, vp]
+    L.muon_group_step.restype = i
+    L.muon_step.argtypes = [ctypes.POINTER(Matrix), i, f, f, i, i, ctypes.POINTER(Options), vp]
+    L.muon_step.restype = i
+    L.muon_orthogonalize.argtypes = [ctypes.POINTER(vp), ctypes.POINTER(vp), i, i, i, i, i,
+                                     ctypes.POINTER(Options), vp]
+    L.muon_orthogonalize.restype = i
+    L.muon_plan_query.argtypes = [ctypes.POINTER(i), ctypes.POINTER(i), i, i, ctypes.POINTER(Options),
+                                  ctypes.POINTER(PlanBatch), i, ctypes.POINTER(i), ctypes.POINTER(i),
+                                  ctypes.POINTER(ctypes.c_size_t)]
+    L.muon_plan_query.restype = i
+    L.muon_status_string.argtypes = [i]
+    L.muon_status_string.restype = ctypes.c_char_p
+    L.muon_last_error.argtypes = []
+    L.muon_last_error.restype = ctypes.c_char_p
+    L.muon_version.argtypes = []
+    L.muon_version.restype = i
+    L.muon_profile_enable.argtypes = [i]
+    L.muon_profile_enable.restype = i
+    L.muon_profile_read.argtypes = [ctypes.POINTER(ProfileEntry), i, i]
+    L.muon_profile_read.restype = i
+    _LIB = L
+    return L
+
+
+def _check(status: int) -> None:
+    if status != 0:
+        raise MuonError(status, load().muon_last_error().decode(errors="replace"))
+
+
+def _stream(stream) -> ctypes.c_void_p:
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    if isinstance(stream, torch.cuda.Stream):
+        return ctypes.c_void_p(stream.cuda_stream)
+    return ctypes.c_void_p(int(stream))
+
+
+def _matrices(t: torch.Tensor, what: str) -> List[Tuple[int, int, int]]:
+    """(device pointer, rows, cols) of each matrix held by a 2-D or 3-D tensor."""
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{what}: expected a torch.Tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{what}: tensor must be contiguous")
+    if t.dim() == 2:
+        return [(t.data_ptr(), t.shape[0], t.shape[1])]
+    if t.dim() == 3:
+        e, r, c = t.shape
+        step = r * c * t.element_size()
+        return [(t.data_ptr() + k * step, r, c) for k in range(e)]
+    raise ValueError(f"{what}: expected a 2-D matrix or a 3-D [E, M, N] bank, got {tuple(t.shape)}")
+
+
+def _options(nesterov=True, momentum_form="ema", weight_decay=0.0, scale_rule="rms", rms_target=0.2,
+             eps=1e-7, coeffs=None, batch_cap_elems=0, ns_steps=5):
+    o = Options()
+    load().muon_default_options(ctypes.byref(o))
+    o.nesterov = 1 if nesterov else 0
+    o.momentum_form = {"ema": 0, "sgd": 1}[momentum_form]
+    o.weight_decay = weight_decay
+    o.scale_rule = {"rms": 0, "original": 1, "none": 2}[scale_rule]
+    o.rms_target = rms_target
+    o.eps = eps
+    keep = None
+    if coeffs is not None:
+        flat = [float(x) for triple in coeffs for x in triple]
+        if len(flat) != 3 * ns_steps:
+            raise ValueError(f"coeffs must hold ns_steps={ns_steps} triples")
+        keep = (ctypes.c_float * len(flat))(*flat)
+        o.coeffs = ctypes.cast(keep, ctypes.POINTER(ctypes.c_float))
+    o.batch_cap_elems = batch_cap_elems
+    return o, keep
+
+
+def _dtype(t: torch.Tensor) -> int:
+    if t.dtype not in _DTYPES:
+        raise TypeError(f"unsupported dtype {t.dtype}: float32 or bfloat16")
+    return _DTYPES[t.dtype]
+
+
+def muon_group_step(params: Sequence[torch.Tensor], grads: Sequence[torch.Tensor],
+                    momentum: Sequence[torch.Tensor], lr: float, beta: float = 0.95, ns_steps: int = 5,
+                    stream=None) -> None:
+    """C `muon_group_step`: one Muon step over same-shaped matrices with
+    default options. Each list entry is an m x n tensor or an [E, m, n] bank."""
+    P = [x for t in params for x in _matrices(t, "params")]
+    G = [x for t in grads for x in _matrices(t, "grads")]
+    M = [x for t in momentum for x in _matrices(t, "momentum")]
+    if not (len(P) == len(G) == len(M)):
+        raise ValueError("params, grads and momentum hold different numbers of matrices")
+    count = len(P)
+    if count == 0:
+        return
+    m, n = P[0][1], P[0][2]
+    for lst, what in ((P, "params"), (G, "grads"), (M, "momentum")):
+        if any((r, c) != (m, n) for _, r, c in lst):
+            raise ValueError(f"{what}: all matrices of a group must be {m} x {n}")
+    dt = _dtype(params[0])
+    arr = ctypes.c_void_p * count
+    _check(load().muon_group_step(arr(*[p for p, _, _ in P]), arr(*[p for p, _, _ in G]),
+                                  arr(*[p for p, _, _ in M]), count, m, n, lr, beta, ns_steps, dt,
+                                  _stream(stream)))
+
+
+def muon_step(mats: Iterable[Tuple[torch.Tensor, torch.Tensor, torch.Tensor]], lr: float,
+              beta: float = 0.95, ns_steps: int = 5, stream=None, **options) -> None:
+    """C `muon_step`: one Muon step over (param, grad, momentum) triples of
+    any shapes; options as in muon_options (nesterov, momentum_form,
+    weight_decay, scale_rule, rms_target, eps, coeffs, batch_cap_elems)."""
+    rows = []
+    dt = None
+    for (p, g, m) in mats:
+        d = _dtype(p)
+        if dt is None:
+            dt = d
+        elif d != dt:
+            raise TypeError("all params of one call must share a dtype")
+        P, G, M = _matrices(p, "param"), _matrices(g, "grad"), _matrices(m, "momentum")
+        if not (len(P) == len(G) == len(M)):
+            raise ValueError("param, grad and momentum hold different numbers of matrices")
+        for (pp, r, c), (gp, r2, c2), (mp, r3, c3) in zip(P, G, M):
+            if not ((r, c) == (r2, c2) == (r3, c3)):
+                raise ValueError(f"shape mismatch {r}x{c} / {r2}x{c2} / {r3}x{c3}")
+            rows.append(Matrix(pp, gp, mp, r, c))
+    if not rows:
+        return
+    o, keep = _options(ns_steps=ns_steps, **options)
+    arr = (Matrix * len(rows))(*rows)
+    _check(load().muon_step(arr, len(rows), lr, beta, ns_steps, dt, ctypes.byref(o), _stream(stream)))
+    del keep
+
+
+def muon_orthogonalize(inputs: Sequence[torch.Tensor], outputs: Sequence[torch.Tensor], ns_steps: int = 5,
+                       stream=None, eps: float = 1e-7, coeffs=None, batch_cap_elems: int = 0) -> None:
+    """C `muon_orthogonalize`: outputs[i] = NS(inputs[i]) (same shapes)."""
+    I = [x for t in inputs for x in _matrices(t, "inputs")]
+    O = [x for t in outputs for x in _matrices(t, "outputs")]
+    if len(I) != len(O):
+        raise ValueError("inputs and outputs hold different numbers of matrices")
+    if not I:
+        return
+    m, n = I[0][1], I[0][2]
+    if any((r, c) != (m, n) for _, r, c in I + O):
+        raise ValueError("all matrices must share one shape")
+    dt = _dtype(inputs[0])
+    o, keep = _options(eps=eps, coeffs=coeffs, batch_cap_elems=batch_cap_elems, ns_steps=ns_steps)
+    arr = ctypes.c_void_p * len(I)
+    _check(load().muon_orthogonalize(arr(*[p for p, _, _ in I]), arr(*[p for p, _, _ in O]), len(I), m, n,
+                                     ns_steps, dt, ctypes.byref(o), _stream(stream)))
+    del keep
+
+
+def plan_query(shapes: Sequence[Tuple[int, int]], dtype: torch.dtype = torch.bfloat16,
+               batch_cap_elems: int = 0) -> dict:
+    """C `muon_plan_query` (host only): the batches and order muon_step would use."""
+    L = load()
+    n = len(shapes)
+    rows = (ctypes.c_int * max(n, 1))(*[r for r, _ in shapes])
+    cols = (ctypes.c_int * max(n, 1))(*[c for _, c in shapes])
+    o, _ = _options(batch_cap_elems=batch_cap_elems)
+    nb = ctypes.c_int(0)
+    ws = ctypes.c_size_t(0)
+    _check(L.muon_plan_query(rows, cols, n, _DTYPES[dtype], ctypes.byref(o), None, 0, ctypes.byref(nb), None,
+                             ctypes.byref(ws)))
+    batches = (PlanBatch * max(nb.value, 1))()
+    order = (ctypes.c_int * max(n, 1))()
+    _check(L.muon_plan_query(rows, cols, n, _DTYPES[dtype], ctypes.byref(o), batches, nb.value, ctypes.byref(nb),
+                             order, ctypes.byref(ws)))
+    return {"batches": [dict(group=b.group, m=b.m, n=b.n, m_pad=b.m_pad, n_pad=b.n_pad, first=b.first,
+                             count=b.count) for b in batches[:nb.value]],
+            "order": list(order[:n]), "workspace_bytes": ws.value}
+
+
+def profile_enable(on: bool = True) -> bool:
+    return bool(load().muon_profile_enable(1 if on else 0))
+
+
+def profile_read(reset: bool = True) -> dict:
+    """Per kernel kind: launches, total_ms, flops, bytes (waits for the events)."""
+    L = load()
+    buf = (ProfileEntry * 32)()
+    n = L.muon_profile_read(buf, 32, 1 if reset else 0)
+    if n < 0:
+        raise MuonError(-n, L.muon_last_error().decode(errors="replace"))
+    return {e.name.decode(): dict(launches=e.launches, total_ms=e.total_ms, flops=e.flops, bytes=e.bytes)
+            for e in buf[:n]}
+
+
+def version() -> int:
+    return load().muon_version()

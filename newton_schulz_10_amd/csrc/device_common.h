@@ -1,0 +1,57 @@
+// Device helpers shared by the HIP kernels of the batched Muon step.
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+#include <cstdint>
+
+namespace muon {
+
+typedef unsigned short bf16_t;  // bf16 storage
+
+__device__ __forceinline__ float bf16_to_f32(bf16_t h) {
+  return __uint_as_float(static_cast<unsigned>(h) << 16);
+}
+
+// Round to nearest, ties to even; NaN stays NaN (quiet bit set).
+__device__ __forceinline__ bf16_t f32_to_bf16(float f) {
+  unsigned u = __float_as_uint(f);
+  if ((u & 0x7fffffffu) > 0x7f800000u) return static_cast<bf16_t>((u >> 16) | 0x40u);
+  u += 0x7fffu + ((u >> 16) & 1u);
+  return static_cast<bf16_t>(u >> 16);
+}
+
+template <typename T> struct Elem;
+template <> struct Elem<float> {
+  __device__ __forceinline__ static float load(const float* p) { return *p; }
+  __device__ __forceinline__ static void store(float* p, float v) { *p = v; }
+};
+template <> struct Elem<bf16_t> {
+  __device__ __forceinline__ static float load(const bf16_t* p) { return bf16_to_f32(*p); }
+  __device__ __forceinline__ static void store(bf16_t* p, float v) { *p = f32_to_bf16(v); }
+};
+
+// Deterministic sum over a 256-thread block (fixed shuffle tree, then the
+// four wave totals in order). Every thread returns the total.
+__device__ __forceinline__ float block_sum_256(float v, float* red /* >= 4 floats LDS */) {
+  for (int off = 32; off > 0; off >>= 1) v += __shfl_xor(v, off, 64);
+  const int wave = threadIdx.x >> 6;
+  __syncthreads();
+  if ((threadIdx.x & 63) == 0) red[wave] = v;
+  __syncthreads();
+  float t = ((red[0] + red[1]) + red[2]) + red[3];
+  return t;
+}
+
+// Maps the hardware block id to a logical tile id so that each XCD (blocks
+// are dealt round-robin over the 8 XCDs) works on a contiguous range of
+// logical tiles, i.e. on whole matrices, keeping each matrix's operands in
+// one XCD's L2.
+__device__ __forceinline__ int xcd_remap(int bid, int total) {
+  constexpr int kXcd = 8;
+  const int x = bid % kXcd, slot = bid / kXcd;
+  const int base = total / kXcd, rem = total % kXcd;
+  return x * base + (x < rem ? x : rem) + slot;
+}
+
+}  // namespace muon

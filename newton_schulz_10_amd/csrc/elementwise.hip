@@ -1,0 +1,252 @@
+// HBM-bound passes of the batched Muon step: momentum (+ transpose to the
+// wide orientation, cast, Frobenius partial sums), the norm finalize, and
+// the parameter update apply (+ transpose back).
+//
+// Paper: arXiv:2609.21594 section 6.2 (a step updates the momentum, runs
+// the batched NS iteration and applies the update locally), section 6.4
+// step 4 (the update and weight decay are applied by fused elementwise
+// kernels), section 6.6 (transpose first when rows exceed columns),
+// section 7.4 (FP32 optimizer state).
+//
+// Every pass works on 64x64 tiles of the wide (m <= n) orientation. A
+// 256-thread block covers one tile: 16 threads per row, 4 consecutive
+// elements per thread, 4 row passes. Tall matrices go through an LDS tile
+// so that both the original-orientation access and the wide-orientation
+// access are coalesced. Partial sums are per tile, in a fixed order, so
+// the norm does not depend on how matrices are batched.
+#include "device_common.h"
+#include "kernels.h"
+#include "plan.h"
+
+namespace muon {
+
+namespace {
+
+constexpr int T = kEwTile;  // 64
+
+template <typename ST>
+__device__ __forceinline__ void load4(const ST* p, int valid, float v[4]) {
+  // valid: number of in-range elements starting at p (0..4)
+  if (valid == 4 && (reinterpret_cast<uintptr_t>(p) % (4 * sizeof(ST)) == 0)) {
+    if constexpr (sizeof(ST) == 4) {
+      float4 q = *reinterpret_cast<const float4*>(p);
+      v[0] = q.x; v[1] = q.y; v[2] = q.z; v[3] = q.w;
+    } else {
+      uint2 q = *reinterpret_cast<const uint2*>(p);
+      v[0] = bf16_to_f32(q.x & 0xffffu); v[1] = bf16_to_f32(q.x >> 16);
+      v[2] = bf16_to_f32(q.y & 0xffffu); v[3] = bf16_to_f32(q.y >> 16);
+    }
+  } else {
+#pragma unroll
+    for (int e = 0; e < 4; ++e) v[e] = e < valid ? Elem<ST>::load(p + e) : 0.0f;
+  }
+}
+
+template <typename ST>
+__device__ __forceinline__ void store4(ST* p, int valid, const float v[4]) {
+  if (valid == 4 && (reinterpret_cast<uintptr_t>(p) % (4 * sizeof(ST)) == 0)) {
+    if constexpr (sizeof(ST) == 4) {
+      *reinterpret_cast<float4*>(p) = make_float4(v[0], v[1], v[2], v[3]);
+    } else {
+      uint2 q;
+      q.x = f32_to_bf16(v[0]) | (static_cast<unsigned>(f32_to_bf16(v[1])) << 16);
+      q.y = f32_to_bf16(v[2]) | (static_cast<unsigned>(f32_to_bf16(v[3])) << 16);
+      *reinterpret_cast<uint2*>(p) = q;
+    }
+  } else {
+#pragma unroll
+    for (int e = 0; e < 4; ++e)
+      if (e < valid) Elem<ST>::store(p + e, v[e]);
+  }
+}
+
+__device__ __forceinline__ int clamp4(int v) { return v < 0 ? 0 : (v > 4 ? 4 : v); }
+
+// One momentum element: returns the NS input u and updates *b.
+__device__ __forceinline__ float momentum_elem(float g, float& b, const MomentumArgs& a) {
+  if (!a.has_buf) return g;
+  const float nb = fmaf(a.beta, b, a.kg * g);
+  b = nb;
+  return a.nesterov ? fmaf(a.beta, nb, a.kg * g) : nb;
+}
+
+template <typename GT, typename XT>
+__global__ __launch_bounds__(256) void momentum_kernel(EwMats mats, MomentumArgs a) {
+  __shared__ float tile[T][T + 1];
+  __shared__ float red[4];
+  const int mi = blockIdx.y;
+  const int tiles_n = a.n_pad / T;
+  const int ti = blockIdx.x / tiles_n, tj = blockIdx.x % tiles_n;
+  const int tx = threadIdx.x & 15, ty = threadIdx.x >> 4;
+  const GT* g = static_cast<const GT*>(mats.src[mi]);
+  float* buf = mats.buf[mi];
+  XT* x0 = static_cast<XT*>(a.x0) + (size_t)(a.first + mi) * a.mat_x;
+  float ss = 0.0f;
+
+  if (!mats.tr[mi]) {
+    // Stored wide: element (i, j) of the m x n matrix is X0[i][j].
+#pragma unroll
+    for (int p = 0; p < 4; ++p) {
+      const int i = ti * T + ty + 16 * p;
+      const int j = tj * T + tx * 4;
+      float u[4] = {0.f, 0.f, 0.f, 0.f};
+      if (i < a.m) {
+        const int valid = clamp4(a.n - j);
+        float gv[4], bv[4] = {0.f, 0.f, 0.f, 0.f};
+        load4<GT>(g + (size_t)i * a.n + j, valid, gv);
+        if (a.has_buf) load4<float>(buf + (size_t)i * a.n + j, valid, bv);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          if (e < valid) {
+            u[e] = momentum_elem(gv[e], bv[e], a);
+            ss = fmaf(u[e], u[e], ss);
+          }
+        }
+        if (a.has_buf) store4<float>(buf + (size_t)i * a.n + j, valid, bv);
+      }
+      store4<XT>(x0 + (size_t)i * a.n_pad + j, 4, u);
+    }
+  } else {
+    // Stored tall: the original is n x m (rows = wide n, cols = wide m) and
+    // X0[i][j] = u[j][i]. Read a 64x64 original tile coalesced, transpose
+    // through LDS, write the wide tile coalesced.
+#pragma unroll
+    for (int p = 0; p < 4; ++p) {
+      const int r = tj * T + ty + 16 * p;   // original row  = wide column
+      const int c = ti * T + tx * 4;        // original col  = wide row
+      float u[4] = {0.f, 0.f, 0.f, 0.f};
+      if (r < a.n) {
+        const int valid = clamp4(a.m - c);
+        float gv[4], bv[4] = {0.f, 0.f, 0.f, 0.f};
+        load4<GT>(g + (size_t)r * a.m + c, valid, gv);
+        if (a.has_buf) load4<float>(buf + (size_t)r * a.m + c, valid, bv);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          if (e < valid) {
+            u[e] = momentum_elem(gv[e], bv[e], a);
+            ss = fmaf(u[e], u[e], ss);
+          }
+        }
+        if (a.has_buf) store4<float>(buf + (size_t)r * a.m + c, valid, bv);
+      }
+#pragma unroll
+      for (int e = 0; e < 4; ++e) tile[ty + 16 * p][tx * 4 + e] = u[e];
+    }
+    __syncthreads();
+#pragma unroll
+    for (int p = 0; p < 4; ++p) {
+      const int il = ty + 16 * p, jl = tx * 4;
+      float v[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) v[e] = tile[jl + e][il];
+      store4<XT>(x0 + (size_t)(ti * T + il) * a.n_pad + tj * T + jl, 4, v);
+    }
+  }
+  const float tot = block_sum_256(ss, red);
+  if (threadIdx.x == 0) a.partials[(size_t)(a.first + mi) * a.ew_blocks + blockIdx.x] = tot;
+}
+
+__global__ __launch_bounds__(256) void finalize_kernel(FinalizeArgs a) {
+  __shared__ float red[4];
+  const int mi = blockIdx.x;
+  const float* p = a.partials + (size_t)mi * a.ew_blocks;
+  float s = 0.0f;
+  for (int k = threadIdx.x; k < a.ew_blocks; k += 256) s += p[k];
+  const float tot = block_sum_256(s, red);
+  if (threadIdx.x == 0) a.scales[mi] = 1.0f / (sqrtf(tot) + a.eps);
+}
+
+template <typename PT, typename XT>
+__global__ __launch_bounds__(256) void apply_kernel(EwMats mats, ApplyArgs a) {
+  __shared__ float tile[T][T + 1];
+  const int mi = blockIdx.y;
+  const int tiles_n = (a.n_pad) / T;
+  const int ti = blockIdx.x / tiles_n, tj = blockIdx.x % tiles_n;
+  const int tx = threadIdx.x & 15, ty = threadIdx.x >> 4;
+  const XT* x = static_cast<const XT*>(a.x) + (size_t)(a.first + mi) * a.mat_x;
+  const float os = a.use_scale ? a.scales[a.first + mi] : 1.0f;
+  const int tr = mats.tr[mi];
+  const float gamma = a.gamma[tr];
+  PT* dst = static_cast<PT*>(mats.dst[mi]);
+  const PT* src = static_cast<const PT*>(mats.src[mi]);
+
+  if (!tr) {
+#pragma unroll
+    for (int p = 0; p < 4; ++p) {
+      const int i = ti * T + ty + 16 * p;
+      const int j = tj * T + tx * 4;
+      if (i >= a.m) continue;
+      const int valid = clamp4(a.n - j);
+      if (valid == 0) continue;
+      float o[4], pv[4] = {0.f, 0.f, 0.f, 0.f};
+      load4<XT>(x + (size_t)i * a.n_pad + j, 4, o);
+      if (a.mode == 0) load4<PT>(src + (size_t)i * a.n + j, valid, pv);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const float oe = o[e] * os;
+        pv[e] = a.mode == 0 ? fmaf(-gamma, oe, a.alpha * pv[e]) : oe;
+      }
+      store4<PT>(dst + (size_t)i * a.n + j, valid, pv);
+    }
+  } else {
+    // Original is n x m; element (r, c) takes O[c][r].
+#pragma unroll
+    for (int p = 0; p < 4; ++p) {
+      const int il = ty + 16 * p;
+      float o[4];
+      load4<XT>(x + (size_t)(ti * T + il) * a.n_pad + tj * T + tx * 4, 4, o);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) tile[il][tx * 4 + e] = o[e];
+    }
+    __syncthreads();
+#pragma unroll
+    for (int p = 0; p < 4; ++p) {
+      const int r = tj * T + ty + 16 * p;  // original row
+      const int c = ti * T + tx * 4;       // original col
+      if (r >= a.n) continue;
+      const int valid = clamp4(a.m - c);
+      if (valid == 0) continue;
+      float pv[4] = {0.f, 0.f, 0.f, 0.f};
+      if (a.mode == 0) load4<PT>(src + (size_t)r * a.m + c, valid, pv);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const float oe = tile[tx * 4 + e][ty + 16 * p] * os;
+        pv[e] = a.mode == 0 ? fmaf(-gamma, oe, a.alpha * pv[e]) : oe;
+      }
+      store4<PT>(dst + (size_t)r * a.m + c, valid, pv);
+    }
+  }
+}
+
+}  // namespace
+
+hipError_t launch_momentum(const EwMats& mats, const MomentumArgs& a, int src_bf16, int ws_bf16,
+                           hipStream_t s) {
+  if (a.count <= 0) return hipSuccess;
+  dim3 grid(a.ew_blocks, a.count), block(256);
+  if (src_bf16 && ws_bf16) hipLaunchKernelGGL((momentum_kernel<bf16_t, bf16_t>), grid, block, 0, s, mats, a);
+  else if (!src_bf16 && ws_bf16) hipLaunchKernelGGL((momentum_kernel<float, bf16_t>), grid, block, 0, s, mats, a);
+  else if (src_bf16 && !ws_bf16) hipLaunchKernelGGL((momentum_kernel<bf16_t, float>), grid, block, 0, s, mats, a);
+  else hipLaunchKernelGGL((momentum_kernel<float, float>), grid, block, 0, s, mats, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_finalize(const FinalizeArgs& a, hipStream_t s) {
+  if (a.count <= 0) return hipSuccess;
+  hipLaunchKernelGGL(finalize_kernel, dim3(a.count), dim3(256), 0, s, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_apply(const EwMats& mats, const ApplyArgs& a, int p_bf16, int ws_bf16,
+                        hipStream_t s) {
+  if (a.count <= 0) return hipSuccess;
+  const int m_pad = (a.m + T - 1) / T * T;
+  dim3 grid((m_pad / T) * (a.n_pad / T), a.count), block(256);
+  if (p_bf16 && ws_bf16) hipLaunchKernelGGL((apply_kernel<bf16_t, bf16_t>), grid, block, 0, s, mats, a);
+  else if (!p_bf16 && ws_bf16) hipLaunchKernelGGL((apply_kernel<float, bf16_t>), grid, block, 0, s, mats, a);
+  else if (p_bf16 && !ws_bf16) hipLaunchKernelGGL((apply_kernel<bf16_t, float>), grid, block, 0, s, mats, a);
+  else hipLaunchKernelGGL((apply_kernel<float, float>), grid, block, 0, s, mats, a);
+  return hipGetLastError();
+}
+
+}  // namespace muon

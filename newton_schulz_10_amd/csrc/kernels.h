@@ -1,0 +1,101 @@
+// Internal interface between the C ABI layer (muon_api.cpp) and the HIP
+// kernels (elementwise.hip, gemm_bf16.hip, gemm_f32.hip). Not installed.
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+#include <cstddef>
+#include <cstdint>
+
+namespace muon {
+
+// Matrices per elementwise launch: their pointers travel by value in the
+// kernel argument block (no device pointer table, nothing to upload).
+constexpr int kEwChunk = 128;
+
+// Per-chunk matrix table for the momentum / apply passes.
+struct EwMats {
+  const void* src[kEwChunk];  // momentum pass: grad (or NS input); apply: param
+  float* buf[kEwChunk];       // momentum pass: momentum buffer (may be unused)
+  void* dst[kEwChunk];        // apply: param or output matrix
+  unsigned char tr[kEwChunk]; // 1 when the matrix is stored tall (rows > cols)
+};
+
+// Momentum pass: reads each matrix's source (and momentum buffer), writes
+// the buffer, the wide zero-padded NS input X0 = u (rounded to the
+// workspace type) and one fp32 partial sum of u^2 per 64x64 tile.
+struct MomentumArgs {
+  int count;                // matrices in this chunk
+  int m, n;                 // wide shape (m <= n)
+  int m_pad, n_pad;
+  int ew_blocks;            // tiles per matrix
+  int first;                // index of the chunk's first matrix in the batch
+  void* x0;                 // workspace X0 of the batch
+  size_t mat_x;             // elements per padded matrix
+  float* partials;          // [batch matrices][ew_blocks]
+  int has_buf;              // 0: NS input is src itself (orthogonalize)
+  float beta;               // buf' = beta*buf + kg*g
+  float kg;                 // 1-beta (EMA) or 1 (heavy ball)
+  int nesterov;             // u = kg*g + beta*buf' if 1, else buf'
+};
+
+// Norm finalize: scales[i] = 1 / (sqrt(sum_k partials[i][k]) + eps).
+struct FinalizeArgs {
+  int count;
+  int ew_blocks;
+  const float* partials;
+  float* scales;
+  float eps;
+};
+
+// Apply pass: mode 0: p' = alpha*p - gamma[tr]*O; mode 1: out = O.
+// O is the wide workspace matrix, times scales[i] when use_scale.
+struct ApplyArgs {
+  int count;
+  int m, n, n_pad;
+  int first;
+  const void* x;            // workspace holding O
+  size_t mat_x;
+  const float* scales;
+  int use_scale;
+  int mode;
+  float alpha;              // 1 - lr*wd
+  float gamma[2];           // lr*scale for wide [0] and tall [1] members
+};
+
+// Batched NS GEMM roles. All operate on padded wide matrices of a batch,
+// element strides per matrix given below. Symmetric roles compute only the
+// tiles that meet the upper triangle and mirror them.
+enum GemmRole {
+  kGram = 0,    // A   = sc * X X^T                (sc = s_i^2 or 1)
+  kPoly = 1,    // B   = b*A + c*(A A)             (A symmetric)
+  kUpdate = 2   // X'  = sc * (a*X + B X)          (sc = s_i or 1)
+};
+
+struct GemmArgs {
+  const void* x;      // X (Gram and Update operand)
+  const void* a;      // A (Poly operand and epilogue)
+  const void* b;      // B (Update operand)
+  void* out;          // output matrices
+  size_t mat_x;       // elements per padded X (m_pad * n_pad)
+  size_t mat_a;       // elements per padded A or B (m_pad * m_pad)
+  int count;          // matrices in the batch
+  int m, n;           // true wide shape (for flop accounting)
+  int m_pad, n_pad;
+  const float* scales;  // per-matrix s (first iteration) or nullptr
+  float ca, cb, cc;     // quintic coefficients of this step
+};
+
+hipError_t launch_momentum(const EwMats& mats, const MomentumArgs& a, int src_bf16, int ws_bf16,
+                           hipStream_t s);
+hipError_t launch_finalize(const FinalizeArgs& a, hipStream_t s);
+hipError_t launch_apply(const EwMats& mats, const ApplyArgs& a, int p_bf16, int ws_bf16,
+                        hipStream_t s);
+hipError_t launch_gemm_bf16(GemmRole role, const GemmArgs& g, hipStream_t s);
+hipError_t launch_gemm_f32(GemmRole role, const GemmArgs& g, hipStream_t s);
+
+// Algorithmic flops of one launch (nominal: a dense product counts
+// 2*M*N*K even where symmetry halves the executed work).
+double gemm_flops(GemmRole role, const GemmArgs& g);
+
+}  // namespace muon

@@ -1,0 +1,468 @@
+// C ABI of libmuon (include/muon.h): argument validation, planning and the
+// launch sequence of the batched Muon step on the caller's HIP stream.
+//
+// Paper: arXiv:2609.21594 section 6.2 (one step: momentum update, batched
+// NS, local update), section 6.6 (shape groups fused into one batched NS
+// with one workspace per batched invocation, 2^29-element batch cap) and
+// section 6.7 (largest matrices first).
+//
+// Launch sequence per batch, all asynchronous on `stream`:
+//   momentum   (per chunk of <= 128 matrices)  -> X0 = u (wide, padded), partials
+//   finalize                                   -> s_i = 1/(||u_i||_F + eps)
+//   ns_steps x { gram, poly, update }          -> X_k (s_i folded into step 1)
+//   apply      (per chunk)                     -> p' (or out)
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cmath>
+#include <cstdlib>
+#include <cstring>
+#include <map>
+#include <mutex>
+#include <string>
+#include <vector>
+
+#include "kernels.h"
+#include "muon.h"
+#include "plan.h"
+
+namespace muon {
+namespace {
+
+thread_local std::string g_err;
+
+int fail(int code, const std::string& msg) {
+  g_err = msg;
+  return code;
+}
+
+int hip_fail(hipError_t e, const char* where) {
+  std::string m = std::string(where) + ": " + hipGetErrorString(e);
+  g_err = m;
+  return e == hipErrorOutOfMemory ? MUON_ERR_OUT_OF_MEMORY : MUON_ERR_HIP;
+}
+
+// ---- stream-ordered workspace from a library-owned pool per device ------
+
+std::mutex g_pool_mu;
+std::map<int, hipMemPool_t> g_pools;
+
+hipError_t get_pool(int dev, hipMemPool_t* out) {
+  std::lock_guard<std::mutex> lk(g_pool_mu);
+  auto it = g_pools.find(dev);
+  if (it != g_pools.end()) { *out = it->second; return hipSuccess; }
+  hipMemPoolProps props;
+  std::memset(&props, 0, sizeof(props));
+  props.allocType = hipMemAllocationTypePinned;
+  props.handleTypes = hipMemHandleTypeNone;
+  props.location.type = hipMemLocationTypeDevice;
+  props.location.id = dev;
+  hipMemPool_t pool;
+  hipError_t e = hipMemPoolCreate(&pool, &props);
+  if (e != hipSuccess) return e;
+  // Keep freed workspace reserved in the pool between steps.
+  uint64_t thr = ~0ull;
+  e = hipMemPoolSetAttribute(pool, hipMemPoolAttrReleaseThreshold, &thr);
+  if (e != hipSuccess) return e;
+  g_pools[dev] = pool;
+  *out = pool;
+  return hipSuccess;
+}
+
+// ---- optional per-launch event timing -----------------------------------
+
+struct Pending {
+  std::string kind;
+  hipEvent_t e0, e1;
+  double flops, bytes;
+};
+struct ProfTotal { int launches = 0; double ms = 0, flops = 0, bytes = 0; };
+
+std::mutex g_prof_mu;
+bool g_prof_on = false;
+std::vector<Pending> g_pending;
+std::vector<hipEvent_t> g_free_events;
+std::map<std::string, ProfTotal> g_totals;
+std::vector<std::string> g_kind_order;
+
+hipEvent_t take_event() {
+  if (!g_free_events.empty()) { hipEvent_t e = g_free_events.back(); g_free_events.pop_back(); return e; }
+  hipEvent_t e = nullptr;
+  if (hipEventCreate(&e) != hipSuccess) return nullptr;
+  return e;
+}
+
+struct ProfScope {
+  bool on = false;
+  Pending p;
+  hipStream_t s;
+  ProfScope(const char* kind, double flops, double bytes, hipStream_t st) : s(st) {
+    std::lock_guard<std::mutex> lk(g_prof_mu);
+    if (!g_prof_on) return;
+    p.kind = kind; p.flops = flops; p.bytes = bytes;
+    p.e0 = take_event(); p.e1 = take_event();
+    if (!p.e0 || !p.e1) return;
+    on = hipEventRecord(p.e0, s) == hipSuccess;
+  }
+  ~ProfScope() {
+    if (!on) return;
+    std::lock_guard<std::mutex> lk(g_prof_mu);
+    if (hipEventRecord(p.e1, s) == hipSuccess) g_pending.push_back(p);
+  }
+};
+
+// ---- the launch sequence --------------------------------------------------
+
+struct MatRef {
+  void* param;        // param (step) or output (orthogonalize)
+  const void* src;    // grad (step) or input (orthogonalize)
+  float* mom;         // momentum (step) or nullptr
+  int rows, cols;
+};
+
+double update_scale(const muon_options& o, int rows, int cols) {
+  switch (o.scale_rule) {
+    case 0: return (double)o.rms_target * std::sqrt((double)std::max(rows, cols));
+    case 1: return std::sqrt(std::max(1.0, (double)rows / (double)cols));
+    default: return 1.0;
+  }
+}
+
+int run(const std::vector<MatRef>& mats, float lr, float beta, int ns_steps, muon_dtype dtype,
+        const muon_options& o, bool orthogonalize_only, hipStream_t stream) {
+  if (mats.empty()) return MUON_OK;
+  const int num = (int)mats.size();
+  std::vector<int> rows(num), cols(num);
+  for (int i = 0; i < num; ++i) { rows[i] = mats[i].rows; cols[i] = mats[i].cols; }
+  Plan plan;
+  std::string err;
+  int rc = build_plan(rows.data(), cols.data(), num, dtype, o.batch_cap_elems, plan, err);
+  if (rc) return fail(rc, err);
+
+  if (const char* f = std::getenv("MUON_TEST_FAIL_ALLOC"))
+    if (f[0] == '1') return fail(MUON_ERR_OUT_OF_MEMORY, "workspace allocation failed (MUON_TEST_FAIL_ALLOC=1)");
+
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+  hipMemPool_t pool;
+  e = get_pool(dev, &pool);
+  if (e != hipSuccess) return hip_fail(e, "hipMemPoolCreate");
+  void* ws = nullptr;
+  e = hipMallocFromPoolAsync(&ws, plan.workspace_bytes, pool, stream);
+  if (e != hipSuccess) {
+    (void)hipGetLastError();
+    return fail(MUON_ERR_OUT_OF_MEMORY, std::string("workspace allocation of ") +
+                std::to_string(plan.workspace_bytes) + " bytes failed: " + hipGetErrorString(e));
+  }
+
+  const bool bf16 = dtype == MUON_BF16;
+  const size_t es = dtype_size(dtype);
+  char* W = static_cast<char*>(ws);
+  const float kg = o.momentum_form == 0 ? 1.0f - beta : 1.0f;
+  int status = MUON_OK;
+
+  for (const Batch& B : plan.batches) {
+    const Layout L = batch_layout(B.count, B.m_pad, B.n_pad, dtype);
+    void* x0 = W + L.x0;
+    void* x1 = W + L.x1;
+    void* Am = W + L.a;
+    void* Bm = W + L.b;
+    float* partials = reinterpret_cast<float*>(W + L.partials);
+    float* scales = reinterpret_cast<float*>(W + L.scales);
+    const double elems = (double)B.m * B.n;
+
+    // 1. momentum (+ transpose, cast, partial sums)
+    for (int c0 = 0; c0 < B.count && status == MUON_OK; c0 += kEwChunk) {
+      const int cn = std::min(kEwChunk, B.count - c0);
+      EwMats em;
+      std::memset(&em, 0, sizeof(em));
+      for (int k = 0; k < cn; ++k) {
+        const MatRef& r = mats[plan.order[B.first + c0 + k]];
+        em.src[k] = r.src;
+        em.buf[k] = r.mom;
+        em.tr[k] = r.rows > r.cols ? 1 : 0;
+      }
+      MomentumArgs a;
+      a.count = cn; a.m = B.m; a.n = B.n; a.m_pad = B.m_pad; a.n_pad = B.n_pad;
+      a.ew_blocks = L.ew_blocks; a.first = c0; a.x0 = x0; a.mat_x = L.mat_x;
+      a.partials = partials; a.has_buf = orthogonalize_only ? 0 : 1;
+      a.beta = beta; a.kg = kg; a.nesterov = o.nesterov;
+      const double bytes = cn * elems * (orthogonalize_only ? es + es : es + 4 + 4 + es);
+      ProfScope ps("momentum", 0.0, bytes, stream);
+      e = launch_momentum(em, a, bf16, bf16, stream);
+      if (e != hipSuccess) status = hip_fail(e, "momentum kernel launch");
+    }
+    if (status) break;
+
+    // 2. per-matrix Frobenius scale
+    {
+      FinalizeArgs f{B.count, L.ew_blocks, partials, scales, o.eps};
+      ProfScope ps("norm_finalize", 0.0, (double)B.count * L.ew_blocks * 4, stream);
+      e = launch_finalize(f, stream);
+      if (e != hipSuccess) { status = hip_fail(e, "finalize kernel launch"); break; }
+    }
+
+    // 3. NS iterations; the Frobenius scale is folded into the first step.
+    void* X = x0;
+    void* Xn = x1;
+    for (int k = 0; k < ns_steps && status == MUON_OK; ++k) {
+      GemmArgs g;
+      g.mat_x = L.mat_x; g.mat_a = L.mat_a; g.count = B.count;
+      g.m = B.m; g.n = B.n; g.m_pad = B.m_pad; g.n_pad = B.n_pad;
+      g.ca = o.coeffs ? o.coeffs[3 * k + 0] : 3.4445f;
+      g.cb = o.coeffs ? o.coeffs[3 * k + 1] : -4.7750f;
+      g.cc = o.coeffs ? o.coeffs[3 * k + 2] : 2.0315f;
+      const GemmRole roles[3] = {kGram, kPoly, kUpdate};
+      const char* names[3] = {"ns_gram", "ns_poly", "ns_update"};
+      for (int r = 0; r < 3; ++r) {
+        g.x = X; g.a = Am; g.b = Bm;
+        g.out = r == 0 ? Am : (r == 1 ? Bm : Xn);
+        g.scales = (k == 0 && r != 1) ? scales : nullptr;
+        ProfScope ps(names[r], gemm_flops(roles[r], g), 0.0, stream);
+        e = bf16 ? launch_gemm_bf16(roles[r], g, stream) : launch_gemm_f32(roles[r], g, stream);
+        if (e != hipSuccess) { status = hip_fail(e, names[r]); break; }
+      }
+      std::swap(X, Xn);
+    }
+    if (status) break;
+
+    // 4. apply (+ transpose back)
+    for (int c0 = 0; c0 < B.count && status == MUON_OK; c0 += kEwChunk) {
+      const int cn = std::min(kEwChunk, B.count - c0);
+      EwMats em;
+      std::memset(&em, 0, sizeof(em));
+      for (int k = 0; k < cn; ++k) {
+        const MatRef& r = mats[plan.order[B.first + c0 + k]];
+        em.src[k] = r.param;
+        em.dst[k] = r.param;
+        em.tr[k] = r.rows > r.cols ? 1 : 0;
+      }
+      ApplyArgs a;
+      a.count = cn; a.m = B.m; a.n = B.n; a.n_pad = B.n_pad; a.first = c0;
+      a.x = X; a.mat_x = L.mat_x; a.scales = scales; a.use_scale = ns_steps == 0 ? 1 : 0;
+      a.mode = orthogonalize_only ? 1 : 0;
+      a.alpha = (float)(1.0 - (double)lr * (double)o.weight_decay);
+      a.gamma[0] = (float)((double)lr * update_scale(o, B.m, B.n));
+      a.gamma[1] = (float)((double)lr * update_scale(o, B.n, B.m));
+      const double bytes = cn * elems * (orthogonalize_only ? es + es : es + es + es);
+      ProfScope ps("apply", 0.0, bytes, stream);
+      e = launch_apply(em, a, bf16, bf16, stream);
+      if (e != hipSuccess) status = hip_fail(e, "apply kernel launch");
+    }
+    if (status) break;
+  }
+
+  hipError_t ef = hipFreeAsync(ws, stream);
+  if (status == MUON_OK && ef != hipSuccess) status = hip_fail(ef, "hipFreeAsync");
+  return status;
+}
+
+int validate_common(float lr, float beta, int ns_steps, muon_dtype dtype, const muon_options* opts,
+                    muon_options& o) {
+  std::string err;
+  int rc = check_scalars(lr, beta, ns_steps, dtype, err);
+  if (rc) return fail(rc, err);
+  default_options(o);
+  if (opts) {
+    o = *opts;
+    if (o.batch_cap_elems == 0) o.batch_cap_elems = MUON_DEFAULT_BATCH_CAP;
+  }
+  rc = check_options(o, ns_steps, err);
+  if (rc) return fail(rc, err);
+  return MUON_OK;
+}
+
+int validate_mats(const std::vector<MatRef>& mats, muon_dtype dtype, bool orthogonalize_only) {
+  std::string err;
+  const size_t es = dtype_size(dtype);
+  std::vector<Range> ranges;
+  for (int i = 0; i < (int)mats.size(); ++i) {
+    const MatRef& r = mats[i];
+    int rc = check_shape(r.rows, r.cols, err, i);
+    if (rc) return fail(rc, err);
+    const char* pn = orthogonalize_only ? "out" : "params";
+    const char* sn = orthogonalize_only ? "in" : "grads";
+    if ((rc = check_ptr(r.param, pn, i, err))) return fail(rc, err);
+    if ((rc = check_ptr(r.src, sn, i, err))) return fail(rc, err);
+    if (!orthogonalize_only && (rc = check_ptr(r.mom, "momentum", i, err))) return fail(rc, err);
+    const unsigned long long elems = (unsigned long long)r.rows * (unsigned long long)r.cols;
+    const auto lo = [](const void* p) { return (unsigned long long)reinterpret_cast<uintptr_t>(p); };
+    if (orthogonalize_only) {
+      // out may be exactly in (in place); any other overlap is an error.
+      if (r.param != r.src) ranges.push_back({lo(r.src), lo(r.src) + elems * es, sn, i});
+      ranges.push_back({lo(r.param), lo(r.param) + elems * es, pn, i});
+    } else {
+      ranges.push_back({lo(r.param), lo(r.param) + elems * es, pn, i});
+      ranges.push_back({lo(r.src), lo(r.src) + elems * es, sn, i});
+      ranges.push_back({lo(r.mom), lo(r.mom) + elems * 4, "momentum", i});
+    }
+  }
+  int rc = check_no_overlap(ranges, err);
+  if (rc) return fail(rc, err);
+  return MUON_OK;
+}
+
+}  // namespace
+}  // namespace muon
+
+using namespace muon;
+
+extern "C" {
+
+void muon_default_options(muon_options* opts) {
+  if (opts) default_options(*opts);
+}
+
+int muon_step(const muon_matrix* mats, int num, float lr, float beta, int ns_steps, muon_dtype dtype,
+              const muon_options* opts, void* stream) {
+  try {
+    g_err.clear();
+    if (num < 0) return fail(MUON_ERR_INVALID_ARGUMENT, "num < 0");
+    if (num > 0 && !mats) return fail(MUON_ERR_INVALID_ARGUMENT, "mats is NULL");
+    muon_options o;
+    int rc = validate_common(lr, beta, ns_steps, dtype, opts, o);
+    if (rc) return rc;
+    std::vector<MatRef> v(num);
+    for (int i = 0; i < num; ++i)
+      v[i] = MatRef{mats[i].param, mats[i].grad, mats[i].momentum, mats[i].rows, mats[i].cols};
+    rc = validate_mats(v, dtype, false);
+    if (rc) return rc;
+    return run(v, lr, beta, ns_steps, dtype, o, false, static_cast<hipStream_t>(stream));
+  } catch (const std::exception& ex) {
+    return fail(MUON_ERR_HIP, std::string("internal error: ") + ex.what());
+  } catch (...) {
+    return fail(MUON_ERR_HIP, "internal error");
+  }
+}
+
+int muon_group_step(void* const* params, const void* const* grads, float* const* momentum, int count,
+                    int m, int n, float lr, float beta, int ns_steps, muon_dtype dtype, void* stream) {
+  try {
+    g_err.clear();
+    if (count < 0) return fail(MUON_ERR_INVALID_ARGUMENT, "count < 0");
+    if (count > 0 && (!params || !grads || !momentum))
+      return fail(MUON_ERR_INVALID_ARGUMENT, "params, grads or momentum array is NULL");
+    muon_options o;
+    int rc = validate_common(lr, beta, ns_steps, dtype, nullptr, o);
+    if (rc) return rc;
+    if (count > 0) {
+      std::string err;
+      if ((rc = check_shape(m, n, err))) return fail(rc, err);
+    }
+    std::vector<MatRef> v(count);
+    for (int i = 0; i < count; ++i) v[i] = MatRef{params[i], grads[i], momentum[i], m, n};
+    rc = validate_mats(v, dtype, false);
+    if (rc) return rc;
+    return run(v, lr, beta, ns_steps, dtype, o, false, static_cast<hipStream_t>(stream));
+  } catch (const std::exception& ex) {
+    return fail(MUON_ERR_HIP, std::string("internal error: ") + ex.what());
+  } catch (...) {
+    return fail(MUON_ERR_HIP, "internal error");
+  }
+}
+
+int muon_orthogonalize(const void* const* in, void* const* out, int count, int m, int n, int ns_steps,
+                       muon_dtype dtype, const muon_options* opts, void* stream) {
+  try {
+    g_err.clear();
+    if (count < 0) return fail(MUON_ERR_INVALID_ARGUMENT, "count < 0");
+    if (count > 0 && (!in || !out)) return fail(MUON_ERR_INVALID_ARGUMENT, "in or out array is NULL");
+    muon_options o;
+    int rc = validate_common(0.0f, 0.0f, ns_steps, dtype, opts, o);
+    if (rc) return rc;
+    if (count > 0) {
+      std::string err;
+      if ((rc = check_shape(m, n, err))) return fail(rc, err);
+    }
+    std::vector<MatRef> v(count);
+    for (int i = 0; i < count; ++i) v[i] = MatRef{out[i], in[i], nullptr, m, n};
+    rc = validate_mats(v, dtype, true);
+    if (rc) return rc;
+    return run(v, 0.0f, 0.0f, ns_steps, dtype, o, true, static_cast<hipStream_t>(stream));
+  } catch (const std::exception& ex) {
+    return fail(MUON_ERR_HIP, std::string("internal error: ") + ex.what());
+  } catch (...) {
+    return fail(MUON_ERR_HIP, "internal error");
+  }
+}
+
+int muon_plan_query(const int* rows, const int* cols, int num, muon_dtype dtype, const muon_options* opts,
+                    muon_plan_batch* batches, int cap, int* num_batches, int* order, size_t* workspace_bytes) {
+  try {
+    g_err.clear();
+    muon_options o;
+    default_options(o);
+    if (opts) o = *opts;
+    Plan plan;
+    std::string err;
+    int rc = build_plan(rows, cols, num, dtype, o.batch_cap_elems, plan, err);
+    if (rc) return fail(rc, err);
+    if (cap > 0 && !batches) return fail(MUON_ERR_INVALID_ARGUMENT, "batches is NULL with cap > 0");
+    for (int i = 0; i < cap && i < (int)plan.batches.size(); ++i) {
+      const Batch& b = plan.batches[i];
+      batches[i] = muon_plan_batch{b.group, b.m, b.n, b.m_pad, b.n_pad, b.first, b.count};
+    }
+    if (num_batches) *num_batches = (int)plan.batches.size();
+    if (order) std::copy(plan.order.begin(), plan.order.end(), order);
+    if (workspace_bytes) *workspace_bytes = plan.workspace_bytes;
+    return MUON_OK;
+  } catch (...) {
+    return fail(MUON_ERR_HIP, "internal error");
+  }
+}
+
+const char* muon_status_string(int status) {
+  switch (status) {
+    case MUON_OK: return "ok";
+    case MUON_ERR_INVALID_ARGUMENT: return "invalid argument";
+    case MUON_ERR_UNSUPPORTED: return "unsupported";
+    case MUON_ERR_MISALIGNED: return "misaligned pointer";
+    case MUON_ERR_OUT_OF_MEMORY: return "out of memory";
+    case MUON_ERR_HIP: return "HIP error";
+    default: return "unknown status";
+  }
+}
+
+const char* muon_last_error(void) { return g_err.c_str(); }
+
+int muon_version(void) { return 100; }
+
+int muon_profile_enable(int on) {
+  std::lock_guard<std::mutex> lk(g_prof_mu);
+  const int prev = g_prof_on ? 1 : 0;
+  g_prof_on = on != 0;
+  return prev;
+}
+
+int muon_profile_read(muon_profile_entry* out, int cap, int reset) {
+  std::lock_guard<std::mutex> lk(g_prof_mu);
+  int status = 0;
+  for (Pending& p : g_pending) {
+    float ms = 0.0f;
+    hipError_t e = hipEventSynchronize(p.e1);
+    if (e == hipSuccess) e = hipEventElapsedTime(&ms, p.e0, p.e1);
+    if (e != hipSuccess) { status = -MUON_ERR_HIP; g_err = hipGetErrorString(e); }
+    if (!g_totals.count(p.kind)) g_kind_order.push_back(p.kind);
+    ProfTotal& t = g_totals[p.kind];
+    t.launches += 1; t.ms += ms; t.flops += p.flops; t.bytes += p.bytes;
+    g_free_events.push_back(p.e0);
+    g_free_events.push_back(p.e1);
+  }
+  g_pending.clear();
+  if (status) return status;
+  int n = 0;
+  for (const std::string& k : g_kind_order) {
+    if (n < cap && out) {
+      const ProfTotal& t = g_totals[k];
+      std::memset(&out[n], 0, sizeof(out[n]));
+      std::strncpy(out[n].name, k.c_str(), sizeof(out[n].name) - 1);
+      out[n].launches = t.launches; out[n].total_ms = t.ms; out[n].flops = t.flops; out[n].bytes = t.bytes;
+    }
+    ++n;
+  }
+  if (reset) { g_totals.clear(); g_kind_order.clear(); }
+  return n;
+}
+
+}  // extern "C"

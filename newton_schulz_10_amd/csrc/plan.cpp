@@ -1,0 +1,166 @@
+// Host-side planning and argument validation (see plan.h).
+#include "plan.h"
+
+#include <algorithm>
+#include <cmath>
+#include <cstdint>
+#include <map>
+#include <sstream>
+#include <tuple>
+
+namespace muon {
+
+namespace {
+size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
+size_t round_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
+}  // namespace
+
+int pad_granularity(muon_dtype dtype) { return dtype == MUON_BF16 ? 128 : 64; }
+
+size_t dtype_size(muon_dtype dtype) { return dtype == MUON_BF16 ? 2 : 4; }
+
+Layout batch_layout(int count, int m_pad, int n_pad, muon_dtype dtype) {
+  Layout L;
+  const size_t es = dtype_size(dtype);
+  const size_t A = 512;
+  L.mat_x = (size_t)m_pad * (size_t)n_pad;
+  L.mat_a = (size_t)m_pad * (size_t)m_pad;
+  L.ew_blocks = (m_pad / kEwTile) * (n_pad / kEwTile);
+  size_t off = 0;
+  L.x0 = off;       off = align_up(off + (size_t)count * L.mat_x * es, A);
+  L.x1 = off;       off = align_up(off + (size_t)count * L.mat_x * es, A);
+  L.a = off;        off = align_up(off + (size_t)count * L.mat_a * es, A);
+  L.b = off;        off = align_up(off + (size_t)count * L.mat_a * es, A);
+  L.partials = off; off = align_up(off + (size_t)count * (size_t)L.ew_blocks * sizeof(float), A);
+  L.scales = off;   off = align_up(off + (size_t)count * sizeof(float), A);
+  L.total = off;
+  return L;
+}
+
+int check_shape(int m, int n, std::string& err, int index) {
+  if (m < 1 || n < 1 || m > MUON_MAX_DIM || n > MUON_MAX_DIM) {
+    std::ostringstream s;
+    s << "matrix";
+    if (index >= 0) s << " " << index;
+    s << ": shape " << m << " x " << n << " outside [1, " << MUON_MAX_DIM << "]";
+    err = s.str();
+    return MUON_ERR_INVALID_ARGUMENT;
+  }
+  return MUON_OK;
+}
+
+int build_plan(const int* rows, const int* cols, int num, muon_dtype dtype, size_t cap,
+               Plan& out, std::string& err) {
+  out = Plan();
+  if (num < 0) { err = "num < 0"; return MUON_ERR_INVALID_ARGUMENT; }
+  if (num > 0 && (!rows || !cols)) { err = "rows/cols array is NULL"; return MUON_ERR_INVALID_ARGUMENT; }
+  if (dtype != MUON_F32 && dtype != MUON_BF16) { err = "unknown dtype"; return MUON_ERR_INVALID_ARGUMENT; }
+  if (cap == 0) cap = MUON_DEFAULT_BATCH_CAP;
+  out.transposed.resize(num);
+  // key = (min, max); groups keep first-appearance order of their matrices.
+  std::map<std::pair<int, int>, std::vector<int>> groups;
+  for (int i = 0; i < num; ++i) {
+    int rc = check_shape(rows[i], cols[i], err, i);
+    if (rc) return rc;
+    out.transposed[i] = rows[i] > cols[i] ? 1 : 0;
+    groups[{std::min(rows[i], cols[i]), std::max(rows[i], cols[i])}].push_back(i);
+  }
+  // Descending element count (large matrices first); ties: larger long
+  // side first, then larger short side.
+  std::vector<std::pair<std::pair<int, int>, std::vector<int>>> g(groups.begin(), groups.end());
+  std::stable_sort(g.begin(), g.end(), [](const auto& x, const auto& y) {
+    long long ex = (long long)x.first.first * x.first.second;
+    long long ey = (long long)y.first.first * y.first.second;
+    if (ex != ey) return ex > ey;
+    if (x.first.second != y.first.second) return x.first.second > y.first.second;
+    return x.first.first > y.first.first;
+  });
+  const int pg = pad_granularity(dtype);
+  size_t ws = 0;
+  for (size_t gi = 0; gi < g.size(); ++gi) {
+    const int m = g[gi].first.first, n = g[gi].first.second;
+    const std::vector<int>& idx = g[gi].second;
+    const int cnt = (int)idx.size();
+    const size_t per_mat = (size_t)m * (size_t)n;
+    size_t per_batch = std::max<size_t>(1, cap / per_mat);
+    int nb = (int)((cnt + per_batch - 1) / per_batch);
+    const int m_pad = (int)round_up(m, pg), n_pad = (int)round_up(n, pg);
+    int start = 0;
+    for (int b = 0; b < nb; ++b) {
+      int c = cnt / nb + (b < cnt % nb ? 1 : 0);  // balanced sizes
+      Batch B{(int)gi, m, n, m_pad, n_pad, (int)out.order.size(), c};
+      for (int k = 0; k < c; ++k) out.order.push_back(idx[start + k]);
+      start += c;
+      out.batches.push_back(B);
+      ws = std::max(ws, batch_layout(c, m_pad, n_pad, dtype).total);
+    }
+  }
+  out.workspace_bytes = ws;
+  return MUON_OK;
+}
+
+void default_options(muon_options& o) {
+  o.nesterov = 1;
+  o.momentum_form = 0;
+  o.weight_decay = 0.0f;
+  o.scale_rule = 0;
+  o.rms_target = 0.2f;
+  o.eps = 1e-7f;
+  o.coeffs = nullptr;
+  o.batch_cap_elems = MUON_DEFAULT_BATCH_CAP;
+}
+
+int check_options(const muon_options& o, int ns_steps, std::string& err) {
+  if (o.nesterov != 0 && o.nesterov != 1) { err = "options.nesterov must be 0 or 1"; return MUON_ERR_INVALID_ARGUMENT; }
+  if (o.momentum_form != 0 && o.momentum_form != 1) { err = "options.momentum_form must be 0 or 1"; return MUON_ERR_INVALID_ARGUMENT; }
+  if (o.scale_rule < 0 || o.scale_rule > 2) { err = "options.scale_rule must be 0, 1 or 2"; return MUON_ERR_INVALID_ARGUMENT; }
+  if (!std::isfinite(o.weight_decay)) { err = "options.weight_decay is not finite"; return MUON_ERR_INVALID_ARGUMENT; }
+  if (!std::isfinite(o.rms_target)) { err = "options.rms_target is not finite"; return MUON_ERR_INVALID_ARGUMENT; }
+  if (!(o.eps >= 0.0f) || !std::isfinite(o.eps)) { err = "options.eps must be finite and >= 0"; return MUON_ERR_INVALID_ARGUMENT; }
+  if (o.coeffs) {
+    for (int i = 0; i < 3 * ns_steps; ++i)
+      if (!std::isfinite(o.coeffs[i])) {
+        std::ostringstream s; s << "options.coeffs[" << i << "] is not finite"; err = s.str();
+        return MUON_ERR_INVALID_ARGUMENT;
+      }
+  }
+  return MUON_OK;
+}
+
+int check_scalars(float lr, float beta, int ns_steps, muon_dtype dtype, std::string& err) {
+  if (!std::isfinite(lr)) { err = "lr is not finite"; return MUON_ERR_INVALID_ARGUMENT; }
+  if (!std::isfinite(beta)) { err = "beta is not finite"; return MUON_ERR_INVALID_ARGUMENT; }
+  if (ns_steps < 0 || ns_steps > MUON_MAX_NS_STEPS) {
+    std::ostringstream s; s << "ns_steps " << ns_steps << " outside [0, " << MUON_MAX_NS_STEPS << "]"; err = s.str();
+    return MUON_ERR_INVALID_ARGUMENT;
+  }
+  if (dtype != MUON_F32 && dtype != MUON_BF16) { err = "unknown dtype"; return MUON_ERR_INVALID_ARGUMENT; }
+  return MUON_OK;
+}
+
+int check_ptr(const void* p, const char* what, int index, std::string& err) {
+  if (!p) {
+    std::ostringstream s; s << what << "[" << index << "] is NULL"; err = s.str();
+    return MUON_ERR_INVALID_ARGUMENT;
+  }
+  if (reinterpret_cast<uintptr_t>(p) % 16 != 0) {
+    std::ostringstream s; s << what << "[" << index << "] is not 16-byte aligned"; err = s.str();
+    return MUON_ERR_MISALIGNED;
+  }
+  return MUON_OK;
+}
+
+int check_no_overlap(std::vector<Range>& r, std::string& err) {
+  std::sort(r.begin(), r.end(), [](const Range& a, const Range& b) { return a.lo < b.lo; });
+  for (size_t i = 1; i < r.size(); ++i) {
+    if (r[i].lo < r[i - 1].hi) {
+      std::ostringstream s;
+      s << r[i - 1].what << "[" << r[i - 1].index << "] overlaps " << r[i].what << "[" << r[i].index << "]";
+      err = s.str();
+      return MUON_ERR_INVALID_ARGUMENT;
+    }
+  }
+  return MUON_OK;
+}
+
+}  // namespace muon

@@ -1,0 +1,76 @@
+// Host-side planning for the batched Muon step: shape grouping, batch
+// splitting, execution order and workspace layout. No HIP dependency, so
+// the planner builds and is tested on a host without a GPU.
+//
+// Source: arXiv:2609.21594 (HyperParallel-FSDP), section 6.6 (matrices are
+// grouped by core shape and fused along a batch axis; tall matrices are
+// transposed first; the NS workspace is allocated once per batched
+// invocation; batches are capped at 2^29 elements) and section 6.7
+// (batches are issued largest matrices first).
+#pragma once
+
+#include <cstddef>
+#include <string>
+#include <vector>
+
+#include "muon.h"
+
+namespace muon {
+
+// Element tile of the momentum/apply passes (wide orientation).
+constexpr int kEwTile = 64;
+
+// One fused batch; m <= n is the group's wide shape.
+struct Batch {
+  int group;
+  int m, n;
+  int m_pad, n_pad;
+  int first;   // offset into Plan::order
+  int count;
+};
+
+struct Plan {
+  std::vector<Batch> batches;             // execution order
+  std::vector<int> order;                 // matrix indices, execution order
+  std::vector<unsigned char> transposed;  // per input matrix: rows > cols
+  size_t workspace_bytes = 0;
+};
+
+// Byte offsets of one batch's workspace regions (each 512-byte aligned).
+struct Layout {
+  size_t x0 = 0, x1 = 0, a = 0, b = 0, partials = 0, scales = 0, total = 0;
+  size_t mat_x = 0;     // elements per padded m_pad x n_pad matrix
+  size_t mat_a = 0;     // elements per padded m_pad x m_pad matrix
+  int ew_blocks = 0;    // elementwise tiles per matrix
+};
+
+// Padding granularity of the GEMM kernels for a dtype (rows and columns of
+// the wide matrix are rounded up to it; the padding holds zeros, which the
+// NS iteration keeps at zero).
+int pad_granularity(muon_dtype dtype);
+size_t dtype_size(muon_dtype dtype);
+
+Layout batch_layout(int count, int m_pad, int n_pad, muon_dtype dtype);
+
+// Groups matrices by {min, max}, orders groups by descending rows*cols,
+// splits each group into balanced batches of at most `cap` elements.
+// Returns MUON_OK or MUON_ERR_INVALID_ARGUMENT with `err` set.
+int build_plan(const int* rows, const int* cols, int num, muon_dtype dtype, size_t cap,
+               Plan& out, std::string& err);
+
+// Option defaults and validation.
+void default_options(muon_options& o);
+int check_options(const muon_options& o, int ns_steps, std::string& err);
+
+// Argument checks shared by the entry points (no device access).
+int check_scalars(float lr, float beta, int ns_steps, muon_dtype dtype, std::string& err);
+int check_shape(int m, int n, std::string& err, int index = -1);
+int check_ptr(const void* p, const char* what, int index, std::string& err);
+
+// Address ranges of the matrices must not overlap (params, grads, momentum
+// of all matrices). `ranges` is a list of [begin, end) byte ranges with a
+// label for the message.
+struct Range { unsigned long long lo, hi; const char* what; int index; };
+int check_no_overlap(std::vector<Range>& ranges, std::string& err);
+
+}  // namespace muon

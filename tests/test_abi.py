@@ -1,0 +1,186 @@
+"""CPU tests of the C ABI: the library loads and exports every symbol that
+include/muon.h declares, the host-only planner, and argument validation
+(every call here is rejected before any HIP call, so no GPU is needed)."""
+import ctypes
+import os
+import re
+import shutil
+import subprocess
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "muon.h")
+
+
+@pytest.fixture(scope="module")
+def lib():
+    import newton_schulz_10_amd as nsa
+    if not os.path.exists(nsa.library_path()):
+        from newton_schulz_10_amd import build
+        build.build_library()
+    return nsa.load()
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(muon_[a-z_]+)\s*\(", text)))
+
+
+def test_header_declares_the_expected_entry_points():
+    names = declared_functions()
+    for n in ("muon_group_step", "muon_step", "muon_orthogonalize", "muon_plan_query", "muon_last_error"):
+        assert n in names
+
+
+def test_library_exports_every_declared_symbol(lib):
+    missing = [n for n in declared_functions() if not hasattr(lib, n)]
+    assert not missing, missing
+    nm = shutil.which("nm")
+    if nm:
+        out = subprocess.run([nm, "-D", "--defined-only", lib._name], capture_output=True, text=True).stdout
+        exported = set(re.findall(r"\bT (muon_\w+)", out))
+        assert set(declared_functions()) <= exported
+
+
+def test_python_binding_names_match_c(lib):
+    import newton_schulz_10_amd as nsa
+    for n in ("muon_group_step", "muon_step", "muon_orthogonalize"):
+        assert callable(getattr(nsa, n))
+    assert set(nsa.SYMBOLS) == set(declared_functions())
+
+
+def test_status_strings_and_version(lib):
+    assert lib.muon_status_string(0) == b"ok"
+    assert lib.muon_status_string(3) == b"misaligned pointer"
+    assert lib.muon_version() >= 100
+
+
+def test_cpp_planner_under_sanitizers(tmp_path):
+    gxx = shutil.which("g++")
+    if not gxx:
+        pytest.skip("g++ not available")
+    exe = str(tmp_path / "test_plan")
+    cmd = [gxx, "-std=c++17", "-O1", "-g", "-fsanitize=address,undefined", "-fno-omit-frame-pointer",
+           "-I", os.path.join(ROOT, "include"), "-I", os.path.join(ROOT, "newton_schulz_10_amd", "csrc"),
+           os.path.join(ROOT, "tests", "cpp", "test_plan.cpp"),
+           os.path.join(ROOT, "newton_schulz_10_amd", "csrc", "plan.cpp"), "-o", exe]
+    subprocess.run(cmd, check=True)
+    env = dict(os.environ, ASAN_OPTIONS="detect_leaks=1", UBSAN_OPTIONS="halt_on_error=1")
+    r = subprocess.run([exe], capture_output=True, text=True, env=env)
+    assert r.returncode == 0, r.stdout + r.stderr
+    assert "planner tests: ok" in r.stdout
+
+
+# ---- plan through the library ---------------------------------------------
+
+def test_plan_query_moe_bank(lib):
+    import torch
+    import newton_schulz_10_amd as nsa
+    shapes = [(2048, 1408)] * 256 + [(1408, 2048)] * 256
+    plan = nsa.plan_query(shapes, torch.bfloat16)
+    assert [b["count"] for b in plan["batches"]] == [171, 171, 170]
+    assert all(b["m"] == 1408 and b["n"] == 2048 for b in plan["batches"])
+    assert plan["order"] == list(range(512))
+    assert plan["workspace_bytes"] > 171 * 1408 * 2048 * 2 * 2
+
+
+def test_plan_query_mlp_and_stack(lib):
+    import torch
+    import newton_schulz_10_amd as nsa
+    mlp = nsa.plan_query([(4096, 14336)] * 32 + [(14336, 4096)] * 32, torch.bfloat16)
+    assert [b["count"] for b in mlp["batches"]] == [8] * 8
+    stack = nsa.plan_query([(7168, 7168)] * 4 + [(7168, 18432)] * 2 + [(7168, 2048)] * 128, torch.bfloat16)
+    assert [(b["m"], b["n"], b["count"]) for b in stack["batches"]] == \
+        [(7168, 18432, 2), (7168, 7168, 4)] + [(2048, 7168, 32)] * 4
+    attn = nsa.plan_query([(2048, 2048)] * 32, torch.bfloat16)
+    assert [b["count"] for b in attn["batches"]] == [32]
+    capped = nsa.plan_query([(2048, 2048)] * 32, torch.bfloat16, batch_cap_elems=5 * 2048 * 2048)
+    assert [b["count"] for b in capped["batches"]] == [5, 5, 5, 5, 4, 4, 4]
+
+
+# ---- validation: rejected before any device access -------------------------
+
+def _fake(addr):
+    return ctypes.c_void_p(addr)
+
+
+def _call_step(lib, mats, lr=0.02, beta=0.95, steps=5, dtype=1, opts=None):
+    import newton_schulz_10_amd as nsa
+    arr = (nsa.Matrix * max(len(mats), 1))(*[nsa.Matrix(*m) for m in mats])
+    o = None if opts is None else ctypes.byref(opts)
+    rc = lib.muon_step(arr if mats else None, len(mats), lr, beta, steps, dtype, o, None)
+    return rc, lib.muon_last_error().decode()
+
+
+BASE = 0x7f0000000000
+
+
+def test_validation_rejects_bad_arguments(lib):
+    import newton_schulz_10_amd as nsa
+    good = (BASE, BASE + 0x100000, BASE + 0x200000, 16, 32)
+    assert _call_step(lib, [good], steps=65)[0] == 1
+    assert _call_step(lib, [good], steps=-1)[0] == 1
+    assert _call_step(lib, [good], lr=float("nan"))[0] == 1
+    assert _call_step(lib, [good], beta=float("inf"))[0] == 1
+    assert _call_step(lib, [good], dtype=9)[0] == 1
+    rc, msg = _call_step(lib, [good, (BASE + 0x300000, 0, BASE + 0x400000, 16, 32)])
+    assert rc == 1 and "grads[1]" in msg
+    rc, msg = _call_step(lib, [good, (BASE + 0x300008, BASE + 0x310000, BASE + 0x400000, 16, 32)])
+    assert rc == 3 and "params[1]" in msg
+    rc, msg = _call_step(lib, [(BASE, BASE + 0x100000, BASE + 0x200000, 0, 32)])
+    assert rc == 1 and "shape" in msg
+    rc, msg = _call_step(lib, [(BASE, BASE + 0x100000, BASE + 0x200000, 16, (1 << 20) + 1)])
+    assert rc == 1
+    # params of matrix 0 overlap the grads of matrix 1
+    rc, msg = _call_step(lib, [good, (BASE + 0x300000, BASE + 0x200, BASE + 0x400000, 16, 32)])
+    assert rc == 1 and "overlaps" in msg
+    # bad options
+    o = nsa.Options()
+    lib.muon_default_options(ctypes.byref(o))
+    o.scale_rule = 5
+    assert _call_step(lib, [good], opts=o)[0] == 1
+    lib.muon_default_options(ctypes.byref(o))
+    o.eps = -1.0
+    assert _call_step(lib, [good], opts=o)[0] == 1
+    lib.muon_default_options(ctypes.byref(o))
+    bad = (ctypes.c_float * 15)(*([1.0] * 14 + [float("nan")]))
+    o.coeffs = ctypes.cast(bad, ctypes.POINTER(ctypes.c_float))
+    rc, msg = _call_step(lib, [good], opts=o)
+    assert rc == 1 and "coeffs[14]" in msg
+    # num < 0 and NULL table
+    assert lib.muon_step(None, -1, 0.02, 0.95, 5, 1, None, None) == 1
+    assert lib.muon_step(None, 2, 0.02, 0.95, 5, 1, None, None) == 1
+
+
+def test_empty_calls_are_noops(lib):
+    # count == 0 returns before any device work.
+    assert lib.muon_step(None, 0, 0.02, 0.95, 5, 1, None, None) == 0
+    assert lib.muon_group_step(None, None, None, 0, 4, 4, 0.02, 0.95, 5, 1, None) == 0
+    assert lib.muon_orthogonalize(None, None, 0, 4, 4, 5, 1, None, None) == 0
+
+
+def test_group_step_and_orthogonalize_validation(lib):
+    arr = ctypes.c_void_p * 2
+    p = arr(BASE, BASE + 0x10000)
+    g = arr(BASE + 0x20000, BASE + 0x30000)
+    m = arr(BASE + 0x40000, BASE + 0x50000)
+    assert lib.muon_group_step(p, g, m, 2, 0, 4, 0.02, 0.95, 5, 1, None) == 1
+    assert lib.muon_group_step(None, g, m, 2, 4, 4, 0.02, 0.95, 5, 1, None) == 1
+    same = arr(BASE, BASE)  # two params at one address
+    assert lib.muon_group_step(same, g, m, 2, 4, 4, 0.02, 0.95, 5, 1, None) == 1
+    ins = arr(BASE, BASE + 0x10000)
+    outs = arr(BASE + 8, BASE + 0x20000)
+    assert lib.muon_orthogonalize(ins, outs, 2, 4, 4, 5, 1, None, None) == 3
+    outs = arr(BASE + 0x10, BASE + 0x20000)  # partial overlap of in[0] and out[0]
+    assert lib.muon_orthogonalize(ins, outs, 2, 4, 4, 5, 1, None, None) == 1
+
+
+def test_alloc_failure_injection_is_host_side(lib, monkeypatch):
+    # With MUON_TEST_FAIL_ALLOC=1 the call reports out-of-memory after
+    # validation and before touching the device.
+    monkeypatch.setenv("MUON_TEST_FAIL_ALLOC", "1")
+    good = (BASE, BASE + 0x100000, BASE + 0x200000, 16, 32)
+    rc, msg = _call_step(lib, [good])
+    assert rc == 4 and "MUON_TEST_FAIL_ALLOC" in msg

@@ -1,0 +1,267 @@
+"""GPU parity: the HIP path (through the C ABI) against the fp64 oracle on
+the same seeded, stored inputs, plus bitwise invariants of the batched
+design. Tolerances: relative Frobenius error of the update <= 1e-4 on the
+float32 path and <= 2e-2 on the bf16 path; momentum <= 1e-6."""
+import numpy as np
+import pytest
+
+import oracle
+import workloads
+from gpu_helpers import (BF16_TOL, F32_TOL, MOM_TOL, check_update, from_device, oracle_case, rel_fro,
+                         to_device, upload_case)
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def nsa():
+    import torch
+    import newton_schulz_10_amd as m
+    m.load()
+    torch.cuda.init()
+    return m
+
+
+def _print(*a):
+    print(*a, flush=True)
+
+
+def run_case(nsa, case, dtype, lr=0.02, beta=0.95, ns_steps=5, **opts):
+    import torch
+    P, G, M = upload_case(case, dtype)
+    nsa.muon_step(list(zip(P, G, M)), lr, beta, ns_steps, **opts)
+    torch.cuda.synchronize()
+    return [from_device(p) for p in P], [from_device(m) for m in M]
+
+
+def assert_parity(case, dtype, p1, m1, ref, tol):
+    worst = 0.0
+    for i, (c, (rp, rb, ro)) in enumerate(zip(case, ref)):
+        p0 = c["params"].as_f64()
+        e = check_update(p0, p1[i], rp, dtype, tol)
+        em = rel_fro(m1[i], rb.astype(np.float32))
+        worst = max(worst, e)
+        assert e <= tol, (i, p0.shape, e)
+        assert em <= MOM_TOL, (i, p0.shape, em)
+        if not np.any(rp - p0):
+            assert np.array_equal(p1[i], p0), i  # zero update must be exact
+    return worst
+
+
+# ---- tiny float32 configuration --------------------------------------------
+
+def test_tiny_fp32_config(nsa):
+    w = workloads.WORKLOADS["tiny_fp32"]
+    case = [dict(grad=workloads.grad(w, gi, j), momentum=workloads.momentum(w, gi, j),
+                 params=workloads.params(w, gi, j)) for gi, j, _, _ in w.matrices()]
+    p1, m1 = run_case(nsa, case, "f32", w.lr, w.beta, w.ns_steps)
+    ref = oracle_case(case, w.lr, w.beta, w.ns_steps)
+    worst = assert_parity(case, "f32", p1, m1, ref, F32_TOL)
+    _print("tiny_fp32 worst rel err", worst)
+
+
+def test_tiny_fp32_closed_form_3x5(nsa):
+    import torch
+    g = np.random.default_rng(0).standard_normal((3, 5)).astype(np.float32)
+    x = torch.from_numpy(g).cuda()
+    out = torch.empty_like(x)
+    nsa.muon_orthogonalize([x], [out], 5)
+    torch.cuda.synchronize()
+    ref = oracle.newton_schulz(g.astype(np.float64))
+    assert rel_fro(from_device(out), ref) <= F32_TOL
+
+
+# ---- small and ragged shapes, several tiles -------------------------------
+
+RAGGED = [(200, 333), (333, 200), (128, 128), (256, 640), (1, 1), (1, 7), (7, 1), (64, 128),
+          (130, 300), (129, 1000), (300, 130), (384, 256)]
+
+
+@pytest.mark.parametrize("dtype,tol", [("bf16", BF16_TOL), ("f32", F32_TOL)])
+def test_ragged_shapes(nsa, dtype, tol):
+    case = workloads.random_case(1, RAGGED, dtype, params_init="zero")
+    p1, m1 = run_case(nsa, case, dtype)
+    ref = oracle_case(case, 0.02, 0.95, 5)
+    worst = assert_parity(case, dtype, p1, m1, ref, tol)
+    _print(dtype, "ragged worst rel err", worst)
+
+
+def test_fp32_nonzero_params_and_options(nsa):
+    shapes = [(96, 160), (160, 96), (64, 64)]
+    case = workloads.random_case(2, shapes, "f32")
+    opts = dict(weight_decay=0.1, scale_rule="original", momentum_form="sgd")
+    p1, m1 = run_case(nsa, case, "f32", 0.05, 0.9, 5, **opts)
+    ref = oracle_case(case, 0.05, 0.9, 5, weight_decay=0.1, scale_rule="original", momentum_form="sgd")
+    assert_parity(case, "f32", p1, m1, ref, F32_TOL)
+    p1, m1 = run_case(nsa, case, "f32", 0.05, 0.9, 3, nesterov=False, scale_rule="none")
+    ref = oracle_case(case, 0.05, 0.9, 3, nesterov=False, scale_rule="none")
+    assert_parity(case, "f32", p1, m1, ref, F32_TOL)
+
+
+def test_bf16_nonzero_params_weight_decay(nsa):
+    case = workloads.random_case(3, [(256, 384), (384, 256)], "bf16")
+    p1, m1 = run_case(nsa, case, "bf16", 0.02, 0.95, 5, weight_decay=0.1)
+    ref = oracle_case(case, 0.02, 0.95, 5, weight_decay=0.1)
+    assert_parity(case, "bf16", p1, m1, ref, BF16_TOL)
+
+
+def test_coefficient_table(nsa):
+    table = [(3.0, -3.2, 1.2), (3.4445, -4.775, 2.0315), (2.9, -3.0, 1.1), (3.4, -4.7, 2.0), (1.875, -1.25, 0.375)]
+    for dtype, tol in (("f32", F32_TOL), ("bf16", BF16_TOL)):
+        case = workloads.random_case(4, [(192, 320), (320, 192)], dtype, params_init="zero")
+        p1, m1 = run_case(nsa, case, dtype, coeffs=table)
+        ref = oracle_case(case, 0.02, 0.95, 5, coeffs=table)
+        assert_parity(case, dtype, p1, m1, ref, tol)
+
+
+@pytest.mark.parametrize("steps", [0, 1, 2])
+def test_few_ns_steps(nsa, steps):
+    for dtype, tol in (("f32", F32_TOL), ("bf16", BF16_TOL)):
+        case = workloads.random_case(5, [(128, 256), (100, 60)], dtype, params_init="zero")
+        p1, m1 = run_case(nsa, case, dtype, ns_steps=steps)
+        ref = oracle_case(case, 0.02, 0.95, steps)
+        assert_parity(case, dtype, p1, m1, ref, tol)
+
+
+def test_orthogonalize_entry(nsa):
+    import torch
+    rng = np.random.default_rng(6)
+    for dtype, tol in (("f32", F32_TOL), ("bf16", BF16_TOL)):
+        st = [workloads._store(rng.standard_normal((144, 272)).astype(np.float32) * 1e-3, dtype) for _ in range(3)]
+        ins = [to_device(s, dtype) for s in st]
+        outs = [torch.empty_like(x) for x in ins]
+        nsa.muon_orthogonalize(ins, outs, 5)
+        # in place as well
+        nsa.muon_orthogonalize([ins[2]], [ins[2]], 5)
+        torch.cuda.synchronize()
+        for k, s in enumerate(st):
+            ref = oracle.newton_schulz(s.as_f64())
+            assert rel_fro(from_device(outs[k]), ref) <= tol
+        assert np.array_equal(from_device(ins[2]), from_device(outs[2]))
+
+
+# ---- bitwise invariants of the batched design ------------------------------
+
+def _bits(ts):
+    return [t.detach().cpu().view(-1).view(__import__("torch").int16 if t.element_size() == 2 else __import__("torch").int32).numpy().copy()
+            for t in ts]
+
+
+def test_batch_partition_invariance_and_determinism(nsa):
+    import torch
+    shapes = [(256, 384)] * 6 + [(384, 256)] * 3
+    case = workloads.random_case(7, shapes, "bf16")
+    outs = []
+    for cap in (0, 256 * 384, 3 * 256 * 384, 0):
+        P, G, M = upload_case(case, "bf16")
+        nsa.muon_step(list(zip(P, G, M)), 0.02, 0.95, 5, batch_cap_elems=cap)
+        torch.cuda.synchronize()
+        outs.append(_bits(P) + _bits(M))
+    for o in outs[1:]:
+        for a, b in zip(outs[0], o):
+            assert np.array_equal(a, b)
+
+
+def test_mixed_call_equals_per_group_calls(nsa):
+    import torch
+    shapes = [(256, 640), (128, 128), (640, 256), (128, 128), (200, 100)]
+    case = workloads.random_case(8, shapes, "bf16")
+    P, G, M = upload_case(case, "bf16")
+    nsa.muon_step(list(zip(P, G, M)), 0.02, 0.95, 5)
+    P2, G2, M2 = upload_case(case, "bf16")
+    for idx in ([0, 2], [1, 3], [4]):
+        nsa.muon_step([(P2[i], G2[i], M2[i]) for i in idx], 0.02, 0.95, 5)
+    torch.cuda.synchronize()
+    for a, b in zip(_bits(P) + _bits(M), _bits(P2) + _bits(M2)):
+        assert np.array_equal(a, b)
+
+
+def test_tall_equals_transposed_wide_twin(nsa):
+    import torch
+    case = workloads.random_case(9, [(384, 256)], "bf16")
+    P, G, M = upload_case(case, "bf16")
+    Pt = [P[0].t().contiguous()]
+    Gt = [G[0].t().contiguous()]
+    Mt = [M[0].t().contiguous()]
+    nsa.muon_step(list(zip(P, G, M)), 0.02, 0.95, 5)
+    nsa.muon_step(list(zip(Pt, Gt, Mt)), 0.02, 0.95, 5)
+    torch.cuda.synchronize()
+    assert torch.equal(P[0], Pt[0].t()) and torch.equal(M[0], Mt[0].t())
+
+
+def test_group_step_entry_and_expert_bank(nsa):
+    import torch
+    # [E, M, N] bank: E independent matrices (never flattened).
+    E, r, c = 6, 128, 192
+    case = workloads.random_case(10, [(r, c)] * E, "bf16", params_init="zero")
+    P, G, M = upload_case(case, "bf16")
+    bankP, bankG, bankM = torch.stack(P), torch.stack(G), torch.stack(M)
+    nsa.muon_group_step([bankP], [bankG], [bankM], 0.02, 0.95, 5)
+    nsa.muon_group_step(P, G, M, 0.02, 0.95, 5)
+    torch.cuda.synchronize()
+    for e in range(E):
+        assert torch.equal(bankP[e], P[e]) and torch.equal(bankM[e], M[e])
+    ref = oracle_case(case, 0.02, 0.95, 5)
+    assert_parity(case, "bf16", [from_device(p) for p in P], [from_device(m) for m in M], ref, BF16_TOL)
+
+
+def test_zero_and_nan_matrices(nsa):
+    import torch
+    case = workloads.random_case(11, [(128, 256)] * 3, "bf16", momentum_init="zero", zero=(1,))
+    P, G, M = upload_case(case, "bf16")
+    G[2].view(-1)[17] = float("nan")
+    p_before = [p.clone() for p in P]
+    nsa.muon_step(list(zip(P, G, M)), 0.02, 0.95, 5)
+    torch.cuda.synchronize()
+    assert torch.equal(P[1], p_before[1])           # zero grad and momentum: exact no-op
+    assert torch.count_nonzero(M[1]) == 0
+    assert torch.isnan(P[2].float()).any()          # NaN propagates within its matrix
+    assert torch.isfinite(P[0].float()).all()       # ... and nowhere else
+    ref = oracle_case(case[:1], 0.02, 0.95, 5)
+    assert check_update(case[0]["params"].as_f64(), from_device(P[0]), ref[0][0], "bf16", BF16_TOL) <= BF16_TOL
+
+
+def test_non_default_stream(nsa):
+    import torch
+    case = workloads.random_case(12, [(256, 256)] * 2, "bf16")
+    P, G, M = upload_case(case, "bf16")
+    P2, G2, M2 = upload_case(case, "bf16")
+    torch.cuda.synchronize()
+    s = torch.cuda.Stream()
+    with torch.cuda.stream(s):
+        nsa.muon_step(list(zip(P, G, M)), 0.02, 0.95, 5)
+    s.synchronize()
+    nsa.muon_step(list(zip(P2, G2, M2)), 0.02, 0.95, 5)
+    torch.cuda.synchronize()
+    assert all(torch.equal(a, b) for a, b in zip(P, P2))
+
+
+def test_alloc_failure_leaves_state_unchanged(nsa, monkeypatch):
+    import torch
+    case = workloads.random_case(13, [(128, 256)], "bf16")
+    P, G, M = upload_case(case, "bf16")
+    p0, m0 = P[0].clone(), M[0].clone()
+    monkeypatch.setenv("MUON_TEST_FAIL_ALLOC", "1")
+    with pytest.raises(nsa.MuonError) as ei:
+        nsa.muon_step(list(zip(P, G, M)), 0.02, 0.95, 5)
+    assert ei.value.status == 4
+    torch.cuda.synchronize()
+    assert torch.equal(P[0], p0) and torch.equal(M[0], m0)
+
+
+def test_checkpoint_resume_bitwise(nsa):
+    import torch
+    case = workloads.random_case(14, [(256, 384), (384, 256)], "bf16")
+    P, G, M = upload_case(case, "bf16")
+    for _ in range(2):
+        nsa.muon_step(list(zip(P, G, M)), 0.02, 0.95, 5)
+    saved = [t.cpu().clone() for t in P + M]
+    for _ in range(2):
+        nsa.muon_step(list(zip(P, G, M)), 0.02, 0.95, 5)
+    torch.cuda.synchronize()
+    P2 = [t.cuda() for t in saved[:2]]
+    M2 = [t.cuda() for t in saved[2:]]
+    for _ in range(2):
+        nsa.muon_step(list(zip(P2, G, M2)), 0.02, 0.95, 5)
+    torch.cuda.synchronize()
+    assert all(torch.equal(a, b) for a, b in zip(P + M, P2 + M2))
