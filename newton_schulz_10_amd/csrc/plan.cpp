@@ -15,7 +15,7 @@ size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
 size_t round_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
 }  // namespace
 
-int pad_granularity(muon_dtype dtype) { return dtype == MUON_BF16 ? 128 : 64; }
+int pad_granularity(muon_dtype dtype) { return dtype == MUON_BF16 ? 256 : 64; }
 
 size_t dtype_size(muon_dtype dtype) { return dtype == MUON_BF16 ? 2 : 4; }
 
