@@ -11,15 +11,30 @@ and a 1408x2048 bf16 matrix (512 matrices, grads N(0, 1e-3), 10% of
 experts idle with zero gradients), momentum and params zero-initialised.
 
 Prints one JSON line: metric, value (nominal NS TFLOP/s of the whole step),
-matrices/s, the roofline of the dominant kernel measured with HIP events
-around its launches, and the fp64 oracle timed on a bounded sample on the
-host cores.
+matrices/s, the roofline of the dominant kernel (its algorithmic flops or
+bytes per launch over its average launch time, both measured with HIP
+events recorded around each launch on the library's stream during the
+timed steps), its HBM traffic per launch from the committed rocprofv3
+counter summary when that summary was taken on the current kernel sources,
+and the fp64 oracle timed on a bounded sample on the host cores.
+
+    python bench.py [--steps K --warmup W --workload NAME]
+    python bench.py --summarize TRACE_DIR FETCH_DIR WRITE_DIR
+        writes profiles/<kernel>_<workload>.md from the rocprofv3 outputs of
+        a --kernel-trace --stats run and of --pmc FETCH_SIZE / WRITE_SIZE
+        runs (all with --output-format csv), the counter runs made with
+        --copy-calib so that each counter can be scaled by what it reads for
+        a plain device copy of known size.
 """
 from __future__ import annotations
 
 import argparse
+import csv
+import glob
+import hashlib
 import json
 import os
+import re
 import sys
 import time
 
@@ -29,6 +44,14 @@ sys.path.insert(0, ROOT)
 PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
 PEAK_F32_TFLOPS = 157.3     # MI355X fp32 vector
 PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
+COPY_CALIB_BYTES = 1 << 30  # device-to-device copy used to scale the HBM counters
+METRIC = "Batched Newton-Schulz TFLOP/s and Muon matrices/s (bf16, 1 MI355X)"
+PROFILES = os.path.join(ROOT, "profiles")
+KERNEL_NAMES = {  # rocprofv3 kernel name fragment -> library kernel kind
+    "ns_gemm_bf16<0>": "ns_gram", "ns_gemm_bf16<1>": "ns_poly", "ns_gemm_bf16<2>": "ns_update",
+    "ns_gemm_f32<0>": "ns_gram", "ns_gemm_f32<1>": "ns_poly", "ns_gemm_f32<2>": "ns_update",
+    "momentum_kernel": "momentum", "finalize_kernel": "norm_finalize", "apply_kernel": "apply",
+}
 
 
 def parse():
@@ -38,11 +61,133 @@ def parse():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="moe_bank_2048x1408")
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="oracle sample budget (0 = skip)")
-    ap.add_argument("--profile-steps", type=int, default=2, help="steps timed per kernel with HIP events")
     ap.add_argument("--copy-calib", action="store_true",
-                    help="also run one plain device copy of known size (for HBM counter scaling)")
+                    help="also run one plain 1 GiB device copy (for HBM counter scaling)")
+    ap.add_argument("--summarize", nargs=3, metavar=("TRACE_DIR", "FETCH_DIR", "WRITE_DIR"),
+                    help="write profiles/ summaries from rocprofv3 csv outputs and exit")
     return ap.parse_args()
 
+
+def source_hash() -> str:
+    """Hash of the library's kernel and launch sources (a counter summary
+    taken on other sources no longer describes the kernels)."""
+    h = hashlib.sha256()
+    for p in sorted(glob.glob(os.path.join(ROOT, "newton_schulz_10_amd", "csrc", "*"))):
+        with open(p, "rb") as f:
+            h.update(os.path.basename(p).encode() + b"\0" + f.read())
+    return h.hexdigest()[:16]
+
+
+def kernel_kind(name: str):
+    for frag, kind in KERNEL_NAMES.items():
+        if frag in name:
+            return kind
+    return None
+
+
+# --------------------------------------------------------------------------
+# rocprofv3 output -> profiles/ summary
+# --------------------------------------------------------------------------
+
+def _read_csvs(d: str, suffix: str):
+    rows = []
+    for p in sorted(glob.glob(os.path.join(d, "**", f"*{suffix}"), recursive=True)):
+        with open(p, newline="") as f:
+            rows.extend(csv.DictReader(f))
+    if not rows:
+        raise SystemExit(f"no *{suffix} under {d}")
+    return rows
+
+
+def _counter_per_kind(rows, counter):
+    """Mean counter value (KiB) per dispatch for each library kernel kind,
+    plus the value read for the calibration copy."""
+    per_dispatch = {}
+    for r in rows:
+        if r["Counter_Name"] != counter:
+            continue
+        key = (r["Dispatch_Id"], r["Kernel_Name"])
+        per_dispatch[key] = per_dispatch.get(key, 0.0) + float(r["Counter_Value"])
+    kinds, copy = {}, None
+    for (_, name), v in per_dispatch.items():
+        k = kernel_kind(name)
+        if k:
+            kinds.setdefault(k, []).append(v)
+        elif "copyBuffer" in name or "copy_kernel" in name:
+            copy = v if copy is None else max(copy, v)
+    return {k: sum(v) / len(v) for k, v in kinds.items()}, copy
+
+
+def summarize(trace_dir, fetch_dir, write_dir, workload):
+    stats = _read_csvs(trace_dir, "kernel_stats.csv")
+    fetch, fcopy = _counter_per_kind(_read_csvs(fetch_dir, "counter_collection.csv"), "FETCH_SIZE")
+    write, wcopy = _counter_per_kind(_read_csvs(write_dir, "counter_collection.csv"), "WRITE_SIZE")
+    if not fcopy or not wcopy:
+        raise SystemExit("calibration copy not found in the counter runs (run them with --copy-calib)")
+    f_scale = COPY_CALIB_BYTES / (fcopy * 1024.0)
+    w_scale = COPY_CALIB_BYTES / (wcopy * 1024.0)
+    kinds = {}
+    for r in stats:
+        k = kernel_kind(r["Name"])
+        if not k:
+            continue
+        e = kinds.setdefault(k, {"calls": 0, "total_ns": 0.0})
+        e["calls"] += int(r["Calls"])
+        e["total_ns"] += float(r["TotalDurationNs"])
+    for k, e in kinds.items():
+        e["avg_ms"] = e["total_ns"] / e["calls"] / 1e6
+        e["hbm_read_bytes_per_launch"] = fetch.get(k, 0.0) * 1024.0 * f_scale if k in fetch else None
+        e["hbm_write_bytes_per_launch"] = write.get(k, 0.0) * 1024.0 * w_scale if k in write else None
+    dom = max(kinds, key=lambda k: kinds[k]["total_ns"])
+    data = {"workload": workload, "source_sha256": source_hash(),
+            "calibration": {"copy_bytes": COPY_CALIB_BYTES, "fetch_kib_read": fcopy, "write_kib_read": wcopy,
+                            "fetch_scale": f_scale, "write_scale": w_scale},
+            "dominant": dom, "kernels": kinds}
+    os.makedirs(PROFILES, exist_ok=True)
+    out = os.path.join(PROFILES, f"{dom}_{workload}.md")
+    with open(out, "w") as f:
+        f.write(f"# rocprofv3 summary: {dom} on {workload}\n\n")
+        f.write("Commands (from the repository root on the GPU host, `cd /tmp && export TMPDIR=/tmp` first):\n\n")
+        f.write("```\n")
+        f.write(f"rocprofv3 --kernel-trace --stats --output-format csv -d <TRACE_DIR> -o trace -- "
+                f"python3 bench.py --workload {workload} --steps 3 --warmup 1 --cpu-seconds 0\n")
+        for c, d in (("FETCH_SIZE", "<FETCH_DIR>"), ("WRITE_SIZE", "<WRITE_DIR>")):
+            f.write(f"rocprofv3 --pmc {c} --output-format csv -d {d} -o pmc -- "
+                    f"python3 bench.py --workload {workload} --steps 1 --warmup 0 --cpu-seconds 0 --copy-calib\n")
+        f.write("python3 bench.py --summarize <TRACE_DIR> <FETCH_DIR> <WRITE_DIR>\n```\n\n")
+        f.write(f"Counter scale: a {COPY_CALIB_BYTES >> 20} MiB device copy reads FETCH_SIZE {fcopy:.0f} KiB "
+                f"(x{f_scale:.3f}) and WRITE_SIZE {wcopy:.0f} KiB (x{w_scale:.3f}).\n\n")
+        f.write("| kernel | launches | avg ms | HBM read GB/launch | HBM write GB/launch |\n|---|---|---|---|---|\n")
+        for k, e in sorted(kinds.items(), key=lambda kv: -kv[1]["total_ns"]):
+            rd = e["hbm_read_bytes_per_launch"]
+            wr = e["hbm_write_bytes_per_launch"]
+            f.write(f"| {k} | {e['calls']} | {e['avg_ms']:.4f} | "
+                    f"{'-' if rd is None else f'{rd / 1e9:.4f}'} | {'-' if wr is None else f'{wr / 1e9:.4f}'} |\n")
+        f.write("\nMachine-readable copy (bench.py reads it while `source_sha256` matches the sources):\n\n")
+        f.write("```json\n" + json.dumps(data, indent=1) + "\n```\n")
+    print(out)
+
+
+def load_traffic(workload, kind):
+    """HBM bytes per launch of `kind` from the committed summary, or None
+    when there is none or it was taken on other kernel sources."""
+    for p in glob.glob(os.path.join(PROFILES, f"*_{workload}.md")):
+        with open(p) as f:
+            m = re.search(r"```json\n(.*?)\n```", f.read(), re.S)
+        if not m:
+            continue
+        data = json.loads(m.group(1))
+        if data.get("source_sha256") != source_hash():
+            continue
+        e = data["kernels"].get(kind)
+        if e and e.get("hbm_read_bytes_per_launch") is not None and e.get("hbm_write_bytes_per_launch") is not None:
+            return e["hbm_read_bytes_per_launch"] + e["hbm_write_bytes_per_launch"]
+    return None
+
+
+# --------------------------------------------------------------------------
+# benchmark
+# --------------------------------------------------------------------------
 
 def make_inputs(w):
     """Device tensors, grouped as [E, rows, cols] banks per shape group."""
@@ -110,9 +255,12 @@ def cpu_baseline(w, budget_s):
 
 def main():
     args = parse()
+    if args.summarize:
+        summarize(*args.summarize, args.workload)
+        return
     if args.gpus != 1:
-        print(f"bench.py measures one GPU: --gpus {args.gpus} is not supported (the library runs "
-              f"on one device; see DESIGN.md for how the path would shard).", file=sys.stderr)
+        print(f"bench.py measures one GPU: --gpus {args.gpus} is not supported (the library runs on "
+              f"one device; sharding across GPUs is not built).", file=sys.stderr)
         sys.exit(2)
     import torch
     import newton_schulz_10_amd as nsa
@@ -131,7 +279,12 @@ def main():
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
+    # Timed region. The library records a HIP event pair around each of its
+    # launches on its stream, giving per-kernel times of these same steps.
+    nsa.profile_enable(True)
+    nsa.profile_read(reset=True)
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
     t0 = time.perf_counter()
     e0.record()
     for _ in range(args.steps):
@@ -140,49 +293,48 @@ def main():
     torch.cuda.synchronize()
     wall_ms = (time.perf_counter() - t0) * 1e3 / args.steps
     ms = e0.elapsed_time(e1) / args.steps
-
-    # Per-kernel times with HIP events recorded on the library's stream.
-    nsa.profile_enable(True)
-    nsa.profile_read(reset=True)
-    for _ in range(args.profile_steps):
-        step()
     kinds = nsa.profile_read(reset=True)
     nsa.profile_enable(False)
+
     per_kernel = {k: {"launches": v["launches"], "avg_ms": v["total_ms"] / max(1, v["launches"]),
-                      "total_ms_per_step": v["total_ms"] / args.profile_steps,
+                      "total_ms_per_step": v["total_ms"] / args.steps,
                       "tflops": (v["flops"] / (v["total_ms"] * 1e-3) / 1e12) if v["flops"] and v["total_ms"] else None,
                       "gbs": (v["bytes"] / (v["total_ms"] * 1e-3) / 1e9) if v["bytes"] and v["total_ms"] else None}
                   for k, v in kinds.items()}
     dom = max(kinds, key=lambda k: kinds[k]["total_ms"])
     dv = kinds[dom]
+    avg_launch_ms = dv["total_ms"] / dv["launches"]
+    traffic = load_traffic(w.key, dom)
     if dv["flops"]:
         achieved = dv["flops"] / (dv["total_ms"] * 1e-3) / 1e12
         peak = PEAK_BF16_TFLOPS if w.dtype == "bf16" else PEAK_F32_TFLOPS
         roof = {"bound": "mfma", "achieved": achieved, "peak": peak, "unit": "TFLOP/s", "frac": achieved / peak,
-                "traffic": None, "kernel": dom, "flops_per_launch": dv["flops"] / dv["launches"],
-                "avg_launch_ms": dv["total_ms"] / dv["launches"]}
+                "traffic": traffic, "kernel": dom, "flops_per_launch": dv["flops"] / dv["launches"],
+                "avg_launch_ms": avg_launch_ms}
     else:
         achieved = dv["bytes"] / (dv["total_ms"] * 1e-3) / 1e9
         roof = {"bound": "hbm", "achieved": achieved, "peak": PEAK_HBM_GBS, "unit": "GB/s",
-                "frac": achieved / PEAK_HBM_GBS, "traffic": None, "kernel": dom,
-                "bytes_per_launch": dv["bytes"] / dv["launches"], "avg_launch_ms": dv["total_ms"] / dv["launches"]}
-    gemm_ms = sum(v["total_ms"] for k, v in kinds.items() if k.startswith("ns_")) / args.profile_steps
+                "frac": achieved / PEAK_HBM_GBS, "traffic": traffic, "kernel": dom,
+                "bytes_per_launch": dv["bytes"] / dv["launches"], "avg_launch_ms": avg_launch_ms}
+    gemm_ms = sum(v["total_ms"] for k, v in kinds.items() if k.startswith("ns_")) / args.steps
 
     if args.copy_calib:
-        a = torch.empty(1 << 28, dtype=torch.float32, device="cuda")  # 1 GiB
+        a = torch.empty(COPY_CALIB_BYTES // 4, dtype=torch.float32, device="cuda")
         b = torch.empty_like(a)
         torch.cuda.synchronize()
         b.copy_(a)
         torch.cuda.synchronize()
+        del a, b
 
     cpu = cpu_baseline(w, args.cpu_seconds) if args.cpu_seconds > 0 else None
     value = flops_per_step / (ms * 1e-3) / 1e12
+    peak_step = PEAK_BF16_TFLOPS if w.dtype == "bf16" else PEAK_F32_TFLOPS
     out = {
-        "metric": "Batched Newton-Schulz TFLOP/s and Muon matrices/s (bf16, 1 MI355X)",
+        "metric": METRIC,
         "value": value,
         "unit": "TFLOP/s",
         "matrices_per_s": mats_per_step / (ms * 1e-3),
-        "frac_of_peak": value / (PEAK_BF16_TFLOPS if w.dtype == "bf16" else PEAK_F32_TFLOPS),
+        "frac_of_peak": value / peak_step,
         "ns_gemm_tflops": flops_per_step / (gemm_ms * 1e-3) / 1e12 if gemm_ms else None,
         "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
         "ms_per_step": ms, "wall_ms_per_step": wall_ms,
