@@ -78,6 +78,13 @@ def source_hash() -> str:
     return h.hexdigest()[:16]
 
 
+def nominal_ns_flops(rows: int, cols: int, ns_steps: int) -> int:
+    """Nominal NS flops of one matrix: per iteration X X^T (2 m^2 n), A A
+    (2 m^3) and B X (2 m^2 n), with m <= n after the transpose-first rule."""
+    m, n = min(rows, cols), max(rows, cols)
+    return ns_steps * (4 * m * m * n + 2 * m ** 3)
+
+
 def kernel_kind(name: str):
     for frag, kind in KERNEL_NAMES.items():
         if frag in name:
@@ -147,14 +154,14 @@ def summarize(trace_dir, fetch_dir, write_dir, workload):
     out = os.path.join(PROFILES, f"{dom}_{workload}.md")
     with open(out, "w") as f:
         f.write(f"# rocprofv3 summary: {dom} on {workload}\n\n")
-        f.write("Commands (from the repository root on the GPU host, `cd /tmp && export TMPDIR=/tmp` first):\n\n")
-        f.write("```\n")
+        f.write("Commands on the GPU host ($REPO = repository root):\n\n")
+        f.write("```\ncd /tmp && export TMPDIR=/tmp\n")
         f.write(f"rocprofv3 --kernel-trace --stats --output-format csv -d <TRACE_DIR> -o trace -- "
-                f"python3 bench.py --workload {workload} --steps 3 --warmup 1 --cpu-seconds 0\n")
+                f"python3 $REPO/bench.py --workload {workload} --steps 3 --warmup 1 --cpu-seconds 0\n")
         for c, d in (("FETCH_SIZE", "<FETCH_DIR>"), ("WRITE_SIZE", "<WRITE_DIR>")):
             f.write(f"rocprofv3 --pmc {c} --output-format csv -d {d} -o pmc -- "
-                    f"python3 bench.py --workload {workload} --steps 1 --warmup 0 --cpu-seconds 0 --copy-calib\n")
-        f.write("python3 bench.py --summarize <TRACE_DIR> <FETCH_DIR> <WRITE_DIR>\n```\n\n")
+                    f"python3 $REPO/bench.py --workload {workload} --steps 1 --warmup 0 --cpu-seconds 0 --copy-calib\n")
+        f.write("python3 $REPO/bench.py --summarize <TRACE_DIR> <FETCH_DIR> <WRITE_DIR>\n```\n\n")
         f.write(f"Counter scale: a {COPY_CALIB_BYTES >> 20} MiB device copy reads FETCH_SIZE {fcopy:.0f} KiB "
                 f"(x{f_scale:.3f}) and WRITE_SIZE {wcopy:.0f} KiB (x{w_scale:.3f}).\n\n")
         f.write("| kernel | launches | avg ms | HBM read GB/launch | HBM write GB/launch |\n|---|---|---|---|---|\n")
@@ -243,7 +250,7 @@ def cpu_baseline(w, budget_s):
         p = workloads.params(w, gi, j).as_f64()
         oracle.muon_matrix_step(p, g, b, w.lr, w.beta, w.ns_steps)
         done += 1
-        flops += oracle.nominal_ns_flops(r, c, w.ns_steps)
+        flops += nominal_ns_flops(r, c, w.ns_steps)
         if time.perf_counter() - t0 >= budget_s:
             break
     el = time.perf_counter() - t0
@@ -264,14 +271,13 @@ def main():
         sys.exit(2)
     import torch
     import newton_schulz_10_amd as nsa
-    import oracle  # only for the nominal flop count and the CPU baseline leg
     import workloads
 
     nsa.load()
     w = workloads.WORKLOADS[args.workload]
     banks = make_inputs(w)
     mats_per_step = w.num_matrices
-    flops_per_step = float(sum(oracle.nominal_ns_flops(r, c, w.ns_steps) for _, _, r, c in w.matrices()))
+    flops_per_step = float(sum(nominal_ns_flops(r, c, w.ns_steps) for _, _, r, c in w.matrices()))
 
     def step():
         nsa.muon_step(banks, w.lr, w.beta, w.ns_steps)
