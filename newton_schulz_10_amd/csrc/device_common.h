@@ -13,12 +13,10 @@ __device__ __forceinline__ float bf16_to_f32(bf16_t h) {
   return __uint_as_float(static_cast<unsigned>(h) << 16);
 }
 
-// Round to nearest, ties to even; NaN stays NaN (quiet bit set).
+// Round to nearest, ties to even (gfx950's v_cvt_pk_bf16_f32, which the
+// compiler pairs up for neighbouring conversions); NaN stays NaN.
 __device__ __forceinline__ bf16_t f32_to_bf16(float f) {
-  unsigned u = __float_as_uint(f);
-  if ((u & 0x7fffffffu) > 0x7f800000u) return static_cast<bf16_t>((u >> 16) | 0x40u);
-  u += 0x7fffu + ((u >> 16) & 1u);
-  return static_cast<bf16_t>(u >> 16);
+  return __builtin_bit_cast(bf16_t, static_cast<__bf16>(f));
 }
 
 template <typename T> struct Elem;

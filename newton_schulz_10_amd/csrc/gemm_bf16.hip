@@ -34,8 +34,11 @@
 //    and writes bf16 back in place, and the finished 256 x 256 tile leaves
 //    LDS as coalesced 16 B row stores and, transposed, as the mirror tile
 //    (Gram/Poly) or the X'^T tile (Update).
-//  * One grid covers every tile of every matrix of the batch; block ids are
-//    remapped so each XCD works on whole matrices (L2 reuse).
+//  * One grid covers every tile of every matrix of the batch: one workgroup
+//    per CU looping over a contiguous (per XCD) range of tiles, the CUs'
+//    start times staggered so that their epilogue stores do not all reach
+//    HBM at once (see ns_gemm_bf16 below).
+#include <atomic>
 #include <type_traits>
 
 #include "device_common.h"
@@ -98,19 +101,17 @@ __device__ __forceinline__ unsigned pack2(bf16_t lo, bf16_t hi) {
   return static_cast<unsigned>(lo) | (static_cast<unsigned>(hi) << 16);
 }
 
-template <int ROLE>
-__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1)))
-void ns_gemm_bf16(GemmArgs g) {
-  // Four K-slab stages of [operand P rows | operand Q rows]; reused as the
-  // 256 x 256 bf16 epilogue tile.
-  __shared__ __attribute__((aligned(1024))) bf16_t lds[kStages][2][kStageElems];
+typedef bf16_t Stages[kStages][2][kStageElems];
 
+// One 256 x 256 output tile (`logical` indexes the batch's tiles, matrix
+// major). `lds`: four K-slab stages of [operand P rows | operand Q rows],
+// reused as the 256 x 256 bf16 epilogue tile.
+template <int ROLE>
+__device__ __forceinline__ void gemm_tile(const GemmArgs& g, int logical, Stages& lds) {
   constexpr bool kSym = (ROLE != kUpdate);
   const int tiles_m = g.m_pad / TILE;
   const int tiles_n = kSym ? tiles_m : g.n_pad / TILE;
   const int per_mat = kSym ? tiles_m * (tiles_m + 1) / 2 : tiles_m * tiles_n;
-  const int total = per_mat * g.count;
-  const int logical = xcd_remap(blockIdx.x, total);
   const int mat = logical / per_mat;
   int I, J;
   if (kSym) upper_tile(logical % per_mat, tiles_m, I, J);
@@ -134,7 +135,11 @@ void ns_gemm_bf16(GemmArgs g) {
   P += (size_t)(I * TILE) * K;
   Q += (size_t)(J * TILE) * K;
 
-  const int tid = threadIdx.x;
+  // The thread id passes through an empty asm so that nothing derived from
+  // it is hoisted out of the tile loop of the persistent kernel (those
+  // values would stay live across the main loop and spill).
+  int tid = threadIdx.x;
+  asm volatile("" : "+v"(tid));
   const int lane = tid & 63, wave = tid >> 6;
   const int wm = wave >> 1, wn = wave & 1;   // wave's 128-row / 128-col block
 
@@ -346,6 +351,70 @@ void ns_gemm_bf16(GemmArgs g) {
   }
 }
 
+// One grid covers every tile of every matrix of the batch.
+//  * gridDim.x >= tiles: one tile per workgroup, block ids remapped so that
+//    each XCD (blocks are dealt round-robin over the 8 XCDs) works on a
+//    contiguous range of tiles, i.e. on whole matrices (L2 reuse).
+//  * otherwise (gridDim.x = one workgroup per CU, a multiple of 8): each
+//    workgroup loops over the tiles of its XCD's contiguous range, slot s
+//    taking tiles s, s + slots, ... The slots start a quarter tile apart
+//    (slot % 4): all tiles cost the same, so in lock step every CU would
+//    reach its epilogue at once and the stores of all CUs would queue at
+//    HBM together; staggered, a quarter of the CUs store while the rest
+//    compute. Tile counts per slot differ by at most one, so the offsets
+//    mostly fill time the short slots would idle anyway.
+template <int ROLE>
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1)))
+void ns_gemm_bf16(GemmArgs g) {
+  __shared__ __attribute__((aligned(1024))) Stages lds;
+  constexpr bool kSym = (ROLE != kUpdate);
+  const int tiles_m = g.m_pad / TILE;
+  const int tiles_n = kSym ? tiles_m : g.n_pad / TILE;
+  const int per_mat = kSym ? tiles_m * (tiles_m + 1) / 2 : tiles_m * tiles_n;
+  const int total = per_mat * g.count;
+  int t, t_end, step;
+  if ((int)gridDim.x >= total) {
+    t = xcd_remap(blockIdx.x, total);
+    t_end = t + 1;
+    step = 1;
+  } else {
+    constexpr int kXcd = 8;
+    const int xcd = blockIdx.x % kXcd, slot = blockIdx.x / kXcd;
+    const int base = total / kXcd, rem = total % kXcd;
+    t = xcd * base + (xcd < rem ? xcd : rem) + slot;
+    t_end = xcd * base + (xcd < rem ? xcd : rem) + base + (xcd < rem ? 1 : 0);
+    step = gridDim.x / kXcd;
+    // Quarter-tile offset in units of s_sleep(127) (about 8K cycles): the
+    // main loop costs roughly 16 cycles per unit of K, the epilogue ~8K.
+    const int K = (ROLE == kGram) ? g.n_pad : g.m_pad;
+    const int quarter = (K * 16 + 8000) / 8128;
+    for (int i = 0; i < (slot & 3) * quarter; ++i) __builtin_amdgcn_s_sleep(127);
+  }
+#pragma nounroll
+  for (; t < t_end; t += step) {
+    gemm_tile<ROLE>(g, t, lds);
+    __syncthreads();   // the epilogue's LDS reads are done before the next fills
+  }
+}
+
+// Compute units of the current device (cached per device).
+hipError_t device_cu_count(int* out) {
+  static std::atomic<int> cache[64];
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev >= 0 && dev < 64) {
+    const int c = cache[dev].load(std::memory_order_relaxed);
+    if (c > 0) { *out = c; return hipSuccess; }
+  }
+  int n = 0;
+  e = hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev);
+  if (e != hipSuccess) return e;
+  if (dev >= 0 && dev < 64) cache[dev].store(n, std::memory_order_relaxed);
+  *out = n;
+  return hipSuccess;
+}
+
 }  // namespace
 
 hipError_t launch_gemm_bf16(GemmRole role, const GemmArgs& g, hipStream_t s) {
@@ -356,7 +425,11 @@ hipError_t launch_gemm_bf16(GemmRole role, const GemmArgs& g, hipStream_t s) {
   const long long per = (role == kUpdate) ? (long long)tm * tn : (long long)tm * (tm + 1) / 2;
   const long long total = per * g.count;
   if (total <= 0 || total > 0x7fffffffLL) return hipErrorInvalidValue;
-  dim3 grid((unsigned)total), block(kThreads);
+  int cus = 0;
+  hipError_t e = device_cu_count(&cus);
+  if (e != hipSuccess) return e;
+  const long long persistent = (cus / 8) * 8;
+  dim3 grid((unsigned)(persistent >= 8 && total > persistent ? persistent : total)), block(kThreads);
   switch (role) {
     case kGram: hipLaunchKernelGGL(ns_gemm_bf16<kGram>, grid, block, 0, s, g); break;
     case kPoly: hipLaunchKernelGGL(ns_gemm_bf16<kPoly>, grid, block, 0, s, g); break;
