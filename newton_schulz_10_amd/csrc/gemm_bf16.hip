@@ -9,19 +9,24 @@
 //   Gram   : A  = sc * X X^T          rows of X  . rows of X     (K = n)
 //   Poly   : B  = b*A + c*(A A^T)     rows of A  . rows of A     (K = m)
 //   Update : X' = sc * (a*X + B X)    rows of B  . rows of X^T   (K = m)
-// A and B are symmetric: Gram and Poly compute only the tiles that meet
-// the upper triangle and store each one twice (tile and mirror). Update
-// stores X' and X'^T. sc is the first step's Frobenius scale (s^2 for
-// Gram, s for Update) and 1 afterwards. Accumulation is fp32 on
+// A and B are symmetric: Gram and Poly compute only the tiles on or below
+// the diagonal and store each one twice (tile and mirror). Update stores
+// X' and X'^T. sc is the first step's Frobenius scale (s^2 for Gram, s for
+// Update) and 1 afterwards. Accumulation is fp32 on
 // v_mfma_f32_32x32x16_bf16; each epilogue is formed in fp32 and rounded
 // once to bf16.
 //
 // Design (gfx950, one 256-thread workgroup per CU):
-//  * Output tile 256 x 256; 4 waves (2 x 2), each 128 x 128 = 4 x 4 MFMA
-//    blocks of 32 x 32 (256 fp32 accumulators per lane, in AGPRs).
-//  * K-slabs of 32 in four LDS stages of 32 KiB, filled by direct
-//    global->LDS loads (16 B per lane) three slabs ahead. Rows are 64 B
-//    with the 16 B chunk index XOR-swizzled so the fragment reads
+//  * Output tiles of 256 x 256: 4 waves (2 x 2), each 128 x 128 = 4 x 4
+//    MFMA blocks of 32 x 32 (256 fp32 accumulators per lane, in AGPRs).
+//    m is padded to 128 only: when m_pad = 256 F + 128 the last tile row is
+//    covered by "wide" tiles of 128 x 512 (two column tiles side by side,
+//    waves 1 x 4), which cost the same as a full tile, so the half row
+//    costs half a row of tiles instead of a full one.
+//  * K-slabs of 32 in four LDS stages of 640 rows x 64 B (P rows, then Q
+//    rows; a full tile uses 256 + 256 of them, a wide one 128 + 512),
+//    filled by direct global->LDS loads (16 B per lane) three slabs ahead.
+//    The 16 B chunk index is XOR-swizzled so the fragment reads
 //    (ds_read_b128) are bank-conflict free.
 //  * Fragments are double buffered in registers: the reads of the next
 //    16-deep step are issued before the MFMAs of the current one. One
@@ -31,13 +36,12 @@
 //    stall the wave's MFMA issue behind them.
 //  * Epilogue through LDS: the operand tile of Poly/Update is loaded into
 //    LDS with coalesced direct loads, each wave forms its outputs in fp32
-//    and writes bf16 back in place, and the finished 256 x 256 tile leaves
-//    LDS as coalesced 16 B row stores and, transposed, as the mirror tile
-//    (Gram/Poly) or the X'^T tile (Update).
+//    and writes bf16 back in place, and the finished tile leaves LDS as
+//    coalesced 16 B non-temporal row stores and, transposed, as the mirror
+//    tile (Gram/Poly) or the X'^T tile (Update).
 //  * One grid covers every tile of every matrix of the batch: one workgroup
-//    per CU looping over a contiguous (per XCD) range of tiles, the CUs'
-//    start times staggered so that their epilogue stores do not all reach
-//    HBM at once (see ns_gemm_bf16 below).
+//    per CU looping over a contiguous (per XCD) range of tiles, so each
+//    XCD's L2 serves whole matrices (see ns_gemm_bf16 below).
 #include <atomic>
 #include <type_traits>
 
@@ -50,18 +54,13 @@ namespace {
 
 typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8;
 typedef __attribute__((ext_vector_type(16))) float f32x16;
+typedef __attribute__((ext_vector_type(4))) unsigned u32x4;
 
-constexpr int TILE = 256;            // output tile edge
+constexpr int TILE = 256;            // full tile edge
 constexpr int BK = 32;               // K per LDS stage
 constexpr int kStages = 4;           // LDS stages (fill runs three slabs ahead)
+constexpr int kStageRows = 640;      // P rows + Q rows of a stage (wide tile: 128 + 512)
 constexpr int kThreads = 256;
-constexpr int kStageElems = TILE * BK;   // elements per operand per stage (8 Ki)
-
-__device__ __forceinline__ void upper_tile(int t, int nt, int& I, int& J) {
-  int i = 0, rowlen = nt;
-  while (t >= rowlen) { t -= rowlen; ++i; --rowlen; }
-  I = i; J = i + t;
-}
 
 // Chunk swizzle of the [row][32 k] stages (64 B rows, 4 chunks of 16 B):
 // chunk index XOR g(row). The fragment reads (ds_read_b128, one row per
@@ -71,17 +70,18 @@ __device__ __forceinline__ void upper_tile(int t, int nt, int& I, int& J) {
 // (row mod 4, chunk) pairs differ.
 __device__ __forceinline__ int kswz(int r) { return ((r >> 1) & 3) ^ ((r >> 2) & 3); }
 
-// Chunk swizzle of the 256 x 256 epilogue tile (rows of 32 chunks of 16 B):
-// 32 consecutive rows get 32 distinct chunks (the MFMA-layout writes), and
-// so do the rows 8c + r, c = 0..31 (the column gathers of the transposed
-// store); whole-row reads touch every chunk of one row once.
+// Chunk swizzle of the epilogue tile (rows of 32 or 64 chunks of 16 B; the
+// XOR touches the low 5 bits only): 32 consecutive rows get 32 distinct
+// chunks (the MFMA-layout writes), and so do the rows 8c + r, c = 0..31
+// (the column gathers of the transposed store); whole-row reads touch
+// every chunk of one row once.
 __device__ __forceinline__ int eswz(int i) { return (i & 31) ^ ((i >> 5) & 7); }
 
-// Direct global->LDS loads: lane l's bytes land at lds_dst + size*l. Issued
-// as inline asm so that the compiler does not track them (its conservative
-// LDS-DMA alias tracking would otherwise wait for the fills of later
-// slabs before any LDS read); completion is awaited with explicit vmcnt
-// waits. `lds_dst` must be wave-uniform.
+// Direct global->LDS load: lane l's 16 bytes land at lds_dst + 16*l.
+// Issued as inline asm so that the compiler does not track it (its
+// conservative LDS-DMA alias tracking would otherwise wait for the fills of
+// later slabs before any LDS read); completion is awaited with explicit
+// vmcnt waits. `lds_dst` must be wave-uniform.
 __device__ __forceinline__ unsigned lds_addr(const void* p) {
   return static_cast<unsigned>(reinterpret_cast<uintptr_t>((const __attribute__((address_space(3))) char*)(p)));
 }
@@ -101,24 +101,50 @@ __device__ __forceinline__ unsigned pack2(bf16_t lo, bf16_t hi) {
   return static_cast<unsigned>(lo) | (static_cast<unsigned>(hi) << 16);
 }
 
-typedef bf16_t Stages[kStages][2][kStageElems];
+__device__ __forceinline__ void store_nt(bf16_t* p, uint4 v) {
+  __builtin_nontemporal_store(__builtin_bit_cast(u32x4, v), reinterpret_cast<u32x4*>(p));
+}
 
-// One 256 x 256 output tile (`logical` indexes the batch's tiles, matrix
-// major). `lds`: four K-slab stages of [operand P rows | operand Q rows],
-// reused as the 256 x 256 bf16 epilogue tile.
-template <int ROLE>
-__device__ __forceinline__ void gemm_tile(const GemmArgs& g, int logical, Stages& lds) {
+// s_waitcnt immediates: vmcnt(n) with expcnt/lgkmcnt unconstrained, and
+// vmcnt(n) together with lgkmcnt(0).
+constexpr int vmcnt(int n) { return ((n >> 4) << 14) | (n & 15) | 0x0F70; }
+constexpr int vmcnt_lgkm0(int n) { return ((n >> 4) << 14) | (n & 15) | 0x0070; }
+
+typedef bf16_t Stages[kStages][kStageRows * BK];
+
+// Tile geometry of one batch: F full tile rows of 256 (rows of A/B and X),
+// plus one half row of 128 when m_pad is an odd multiple of 128, covered by
+// wide tiles. Per matrix: `full` tiles, then `wide` tiles.
+struct Geom {
+  int F, half, tn, full, wide, per_mat;
+};
+
+__device__ __forceinline__ Geom geom(const GemmArgs& g, bool sym) {
+  Geom t;
+  t.F = g.m_pad / TILE;
+  t.half = (g.m_pad % TILE) != 0;
+  t.tn = sym ? t.F + t.half : g.n_pad / TILE;   // column tiles (the last may be half)
+  t.full = sym ? t.F * (t.F + 1) / 2 : t.F * t.tn;
+  t.wide = t.half ? (t.tn + 1) / 2 : 0;
+  t.per_mat = t.full + t.wide;
+  return t;
+}
+
+// One output tile. Full (WIDE = false): rows I*256 .. +255, columns
+// J*256 .. +255. Wide: rows I*256 .. +127 (I = F), columns J*256 .. +511.
+// Columns at or beyond `colmax` (the padded width of the output) are
+// computed from clamped loads and never stored. `lds`: the K-slab stages,
+// reused as the epilogue tile.
+template <int ROLE, bool WIDE>
+__device__ __forceinline__ void gemm_tile(const GemmArgs& g, int mat, int I, int J, Stages& lds) {
   constexpr bool kSym = (ROLE != kUpdate);
-  const int tiles_m = g.m_pad / TILE;
-  const int tiles_n = kSym ? tiles_m : g.n_pad / TILE;
-  const int per_mat = kSym ? tiles_m * (tiles_m + 1) / 2 : tiles_m * tiles_n;
-  const int mat = logical / per_mat;
-  int I, J;
-  if (kSym) upper_tile(logical % per_mat, tiles_m, I, J);
-  else { I = (logical % per_mat) / tiles_n; J = (logical % per_mat) % tiles_n; }
+  constexpr int PR = WIDE ? 128 : 256;   // tile rows (P rows)
+  constexpr int QR = WIDE ? 512 : 256;   // tile columns (Q rows)
+  constexpr int RW = (PR + QR) / 4;      // stage rows filled by each wave
+  constexpr int NL = RW / 16;            // 1 KiB fill loads per wave per slab (8 or 10)
+  constexpr int NLh = NL / 2;
 
-  // Operands: output rows come from P, output columns from Q; both are
-  // row-major with K contiguous.
+  const int colmax = kSym ? g.m_pad : g.n_pad;
   const int K = (ROLE == kGram) ? g.n_pad : g.m_pad;
   const bf16_t* P;
   const bf16_t* Q;
@@ -133,7 +159,8 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& g, int logical, Stages
     Q = static_cast<const bf16_t*>(g.xt) + (size_t)mat * g.mat_x;
   }
   P += (size_t)(I * TILE) * K;
-  Q += (size_t)(J * TILE) * K;
+  const int q0 = J * TILE;                 // first Q row (output column)
+  const int qlast = colmax - 1 - q0;       // last valid Q row relative to q0
 
   // The thread id passes through an empty asm so that nothing derived from
   // it is hoisted out of the tile loop of the persistent kernel (those
@@ -141,39 +168,45 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& g, int logical, Stages
   int tid = threadIdx.x;
   asm volatile("" : "+v"(tid));
   const int lane = tid & 63, wave = tid >> 6;
-  const int wm = wave >> 1, wn = wave & 1;   // wave's 128-row / 128-col block
+  // Wave's 128-row block (stage rows of P) and 128-column block (of Q).
+  const int rb0 = WIDE ? 0 : (wave >> 1) * 128;
+  const int cb0 = WIDE ? wave * 128 : (wave & 1) * 128;
 
-  // LDS fill of one K-slab: each wave moves 64 rows of P and 64 of Q in
-  // 8 loads of 1 KiB (16 rows of 64 B each); fill_one(kt, q) issues load q
-  // (0..3: P rows, 4..7: Q rows).
+  // LDS fill of one K-slab: wave w moves stage rows [w*RW, (w+1)*RW) in
+  // loads of 16 rows (1 KiB); fill_one(kt, q) issues load q. Stage rows
+  // below PR are P rows, the rest Q rows.
   const int nk = K / BK;
   const int last = nk - 1;
-  auto fill_one = [&](int kt, int q) {   // q = 0..7
+  auto fill_one = [&](int kt, int q) {
     const int k0 = (kt < last ? kt : last) * BK;   // past the end: repeat the last slab
-    const int st = kt & (kStages - 1);
-    const bf16_t* src = q < 4 ? P : Q;
-    const int rb = wave * 64 + (q & 3) * 16;
+    const int rb = wave * RW + q * 16;
     const int r = rb + (lane >> 2);
     const int ch = (lane & 3) ^ kswz(r);
-    dma16(src + (size_t)r * K + k0 + ch * 8, &lds[st][q >> 2][rb * BK]);
+    const bf16_t* src;
+    if (rb < PR) {
+      src = P + (size_t)r * K;
+    } else {
+      int qr = r - PR;
+      qr = qr < qlast ? qr : qlast;   // rows past the output width: any valid row
+      src = Q + (size_t)(q0 + qr) * K;
+    }
+    dma16(src + k0 + ch * 8, &lds[kt & (kStages - 1)][rb * BK]);
   };
 
   // Fragments of one 16-deep K step: rf = P rows (4 blocks of 32 output
   // rows), cf = Q rows (4 blocks of 32 output columns), 8 bf16 per lane.
   auto read_frags = [&](int kt, int ks, bf16x8 (&rf)[4], bf16x8 (&cf)[4]) {
-    const int st = kt & (kStages - 1);
-    const bf16_t* Ps = lds[st][0];
-    const bf16_t* Qs = lds[st][1];
+    const bf16_t* S = lds[kt & (kStages - 1)];
     const int ch = 2 * ks + (lane >> 5);
 #pragma unroll
     for (int b = 0; b < 4; ++b) {
-      const int r = wm * 128 + b * 32 + (lane & 31);
-      rf[b] = *reinterpret_cast<const bf16x8*>(Ps + r * BK + ((ch ^ kswz(r)) * 8));
+      const int r = rb0 + b * 32 + (lane & 31);
+      rf[b] = *reinterpret_cast<const bf16x8*>(S + r * BK + ((ch ^ kswz(r)) * 8));
     }
 #pragma unroll
     for (int a = 0; a < 4; ++a) {
-      const int r = wn * 128 + a * 32 + (lane & 31);
-      cf[a] = *reinterpret_cast<const bf16x8*>(Qs + r * BK + ((ch ^ kswz(r)) * 8));
+      const int r = PR + cb0 + a * 32 + (lane & 31);
+      cf[a] = *reinterpret_cast<const bf16x8*>(S + r * BK + ((ch ^ kswz(r)) * 8));
     }
   };
 
@@ -189,18 +222,18 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& g, int logical, Stages
   // compute issues fill(j+3) in two halves around its barrier:
   //   fillA(j+3) | barrier j | fillB(j+3).
   // At barrier j the fill of slab j+1 must have landed; the loads issued
-  // after it are fill(j+2) and fillA(j+3): 8 + 4 = 12. Fills past the last
+  // after it are fill(j+2) and fillA(j+3): NL + NLh. Fills past the last
   // slab repeat the last slab (into a stage that is no longer read), which
   // keeps that count exact to the end.
   for (int j = 0; j < kStages - 1; ++j)
-    for (int q = 0; q < 8; ++q) fill_one(j, q);
-  __builtin_amdgcn_s_waitcnt(0x4F70);  // vmcnt(16): fill(0) landed
+    for (int q = 0; q < NL; ++q) fill_one(j, q);
+  __builtin_amdgcn_s_waitcnt(vmcnt(2 * NL));  // fill(0) landed
   lds_barrier();
 
   bf16x8 rf[2][4], cf[2][4];
   read_frags(0, 0, rf[0], cf[0]);
-  // 16 MFMAs of one step; after every 4 an optional hook issues memory
-  // work, so loads never queue up in a burst in front of the MFMAs.
+  // 16 MFMAs of one step; after every 4 a hook issues memory work, so
+  // loads never queue up in a burst in front of the MFMAs.
   auto mfma_step = [&](int cur, auto hook) {
 #pragma unroll
     for (int a = 0; a < 4; ++a) {
@@ -212,6 +245,12 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& g, int logical, Stages
       __builtin_amdgcn_sched_barrier(0);
     }
   };
+  // Loads of fill half h (0: loads 0..NLh-1, 1: NLh..NL-1) issued after
+  // MFMA group a of a step.
+  auto fill_part = [&](int kt, int h, int a) {
+#pragma unroll
+    for (int q = (a * NLh) / 4; q < ((a + 1) * NLh) / 4; ++q) fill_one(kt, h * NLh + q);
+  };
   // One K-slab (two 16-deep steps). `more` (compile-time) says whether a
   // next slab exists; the last slab is peeled so the loop body has no
   // data-dependent branch around LDS reads (the compiler's wait-count
@@ -221,15 +260,15 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& g, int logical, Stages
     read_frags(kt, 1, rf[1], cf[1]);
     __builtin_amdgcn_sched_barrier(0);
     if constexpr (decltype(more)::value) {
-      mfma_step(0, [&](int a) { fill_one(kt + 3, a); });
+      mfma_step(0, [&](int a) { fill_part(kt + 3, 0, a); });
       // This wave's fill of slab kt+1 and its LDS reads have completed;
       // after the barrier, every wave's have, and stage (kt+3) % 4's last
       // readers (slab kt-1) are long done.
-      __builtin_amdgcn_s_waitcnt(0x007C);  // vmcnt(12) lgkmcnt(0)
+      __builtin_amdgcn_s_waitcnt(vmcnt_lgkm0(NL + NLh));
       lds_barrier();
       read_frags(kt + 1, 0, rf[0], cf[0]);
       __builtin_amdgcn_sched_barrier(0);
-      mfma_step(1, [&](int a) { fill_one(kt + 3, 4 + a); });
+      mfma_step(1, [&](int a) { fill_part(kt + 3, 1, a); });
     } else {
       mfma_step(0, [](int) {});
       mfma_step(1, [](int) {});
@@ -239,8 +278,10 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& g, int logical, Stages
   slab(last, std::false_type{});
 
   // ---- epilogue ----------------------------------------------------------
-  // acc[a][b] element v: tile row i = wm*128 + 32b + lane%32, tile columns
-  // j .. j+3 with j = wn*128 + 32a + 8*(v/4) + 4*(lane/32).
+  // acc[a][b] element v: tile row i = rb0 + 32b + lane%32, tile columns
+  // j .. j+3 with j = cb0 + 32a + 8*(v/4) + 4*(lane/32). T is the tile in
+  // LDS, PR rows x QR columns, 16 B chunks swizzled by eswz(row).
+  constexpr int TC8 = QR / 8;   // chunks per tile row
   float sc = 1.0f;
   if (g.scales) {
     const float s = g.scales[mat];
@@ -248,41 +289,45 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& g, int logical, Stages
   }
   const int ldo = (ROLE == kUpdate) ? g.n_pad : g.m_pad;
   bf16_t* out = static_cast<bf16_t*>(g.out) + (size_t)mat * ((ROLE == kUpdate) ? g.mat_x : g.mat_a);
-  bf16_t* T = &lds[0][0][0];   // 256 x 256 bf16, chunk-swizzled rows
+  bf16_t* T = &lds[0][0];
+  auto tidx = [&](int i, int j) { return i * QR + (((j >> 3) ^ eswz(i)) << 3) + (j & 7); };
+  const int valid_cols = colmax - q0 < QR ? colmax - q0 : QR;
 
   __builtin_amdgcn_s_waitcnt(0x0070);  // vmcnt(0) lgkmcnt(0): stages no longer read
   lds_barrier();
 
   if (ROLE == kPoly || ROLE == kUpdate) {
-    // Epilogue operand tile (A for Poly, X for Update) into T: 128 loads of
-    // 1 KiB (two rows each), 32 per wave; lane l of a load takes row
-    // i0 + l/32, stored chunk l%32, i.e. source chunk (l%32) ^ eswz(row).
+    // Epilogue operand tile (A for Poly, X for Update; both ldo wide) into
+    // T: 128 loads of 1 KiB, 32 per wave; lane l of a load takes stored
+    // chunk l % TC8 of its row, i.e. source chunk (l % TC8) ^ eswz(row).
     const bf16_t* E = (ROLE == kPoly)
         ? static_cast<const bf16_t*>(g.a) + (size_t)mat * g.mat_a
         : static_cast<const bf16_t*>(g.x) + (size_t)mat * g.mat_x;
-    E += (size_t)(I * TILE) * ldo + J * TILE;
+    E += (size_t)(I * TILE) * ldo;
+    constexpr int RPI = 1024 / (QR * 2);   // tile rows per load
 #pragma unroll 8
     for (int q = 0; q < 32; ++q) {
-      const int i0 = (wave * 32 + q) * 2;
-      const int i = i0 + (lane >> 5);
-      const int c = (lane & 31) ^ eswz(i);
-      dma16(E + (size_t)i * ldo + c * 8, T + i0 * TILE);
+      const int i0 = (wave * 32 + q) * RPI;
+      const int i = i0 + lane / TC8;
+      int col = q0 + ((lane % TC8) ^ eswz(i)) * 8;
+      col = col < ldo - 8 ? col : ldo - 8;   // columns past the width: any valid ones
+      dma16(E + (size_t)i * ldo + col, T + i0 * QR);
     }
-    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
+    __builtin_amdgcn_s_waitcnt(vmcnt(0));
     lds_barrier();
   }
 
   // Each wave forms its outputs in fp32 and writes bf16 into T.
 #pragma unroll
   for (int b = 0; b < 4; ++b) {
-    const int i = wm * 128 + b * 32 + (lane & 31);
-    bf16_t* row = T + i * TILE;
+    const int i = rb0 + b * 32 + (lane & 31);
+    bf16_t* row = T + i * QR;
     const int sw = eswz(i);
 #pragma unroll
     for (int a = 0; a < 4; ++a) {
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
-        const int j = wn * 128 + a * 32 + 8 * q + 4 * (lane >> 5);
+        const int j = cb0 + a * 32 + 8 * q + 4 * (lane >> 5);
         uint2* p = reinterpret_cast<uint2*>(row + (((j >> 3) ^ sw) << 3) + (j & 7));
         float v[4];
 #pragma unroll
@@ -307,46 +352,61 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& g, int logical, Stages
   }
   __syncthreads();
 
-  auto tidx = [&](int i, int j) { return i * TILE + (((j >> 3) ^ eswz(i)) << 3) + (j & 7); };
-  if (kSym && I == J) {
-    // Diagonal tile: make it exactly symmetric, lower part = upper part
-    // transposed (reads touch only i < j, writes only i > j).
-    for (int idx = tid; idx < TILE * TILE; idx += kThreads) {
-      const int i = idx >> 8, j = idx & 255;
-      if (i > j) T[tidx(i, j)] = T[tidx(j, i)];
+  // Diagonal blocks of A/B (full tile I == J, or the 128 x 128 corner of a
+  // wide tile) are made exactly symmetric: lower part = upper part
+  // transposed (reads touch only i < j, writes only i > j). They have no
+  // mirror elsewhere.
+  int diag_off = -1;   // tile column of the diagonal block, if any
+  if (kSym) {
+    if (!WIDE && I == J) diag_off = 0;
+    if (WIDE && (I == J || I == J + 1)) diag_off = (I - J) * TILE;
+  }
+  constexpr int D = WIDE ? 128 : 256;   // edge of a diagonal block
+  if (diag_off >= 0) {
+    for (int idx = tid; idx < D * D; idx += kThreads) {
+      const int i = idx / D, j = idx % D;
+      if (i > j) T[tidx(i, diag_off + j)] = T[tidx(j, diag_off + i)];
     }
     __syncthreads();
   }
 
-  // Tile rows -> out(I, J): 32 lanes store one 512 B row.
+  // Tile rows -> out: TC8 lanes store one row (non-temporal: the output is
+  // read by the next kernel, not this one).
 #pragma unroll 4
-  for (int r = 0; r < (TILE * TILE / 8) / kThreads; ++r) {
+  for (int r = 0; r < (PR * TC8) / kThreads; ++r) {
     const int id = r * kThreads + tid;
-    const int i = id >> 5, c = id & 31;
-    const uint4 v = *reinterpret_cast<const uint4*>(T + i * TILE + ((c ^ eswz(i)) << 3));
-    *reinterpret_cast<uint4*>(out + (size_t)(I * TILE + i) * ldo + J * TILE + c * 8) = v;
+    const int i = id / TC8, c = id % TC8;
+    if (c * 8 < valid_cols) {
+      const uint4 v = *reinterpret_cast<const uint4*>(T + i * QR + ((c ^ eswz(i)) << 3));
+      store_nt(out + (size_t)(I * TILE + i) * ldo + q0 + c * 8, v);
+    }
   }
 
-  // Transposed tile -> mirror (J, I) of A/B, or tile (J, I) of X'^T.
+  // Transposed tile -> mirror of A/B (output rows = tile columns, except
+  // the diagonal block), or the X'^T tile of Update.
   bf16_t* out2 = nullptr;
   if (kSym) {
-    if (I != J) out2 = out;
+    if (WIDE || I != J) out2 = out;
   } else if (g.out2) {
     out2 = static_cast<bf16_t*>(g.out2) + (size_t)mat * g.mat_x;
   }
   if (out2) {
+    constexpr int RC8 = PR / 8;   // chunks per transposed row
     const int ld2 = g.m_pad;
 #pragma unroll 2
-    for (int r = 0; r < (TILE * TILE / 8) / kThreads; ++r) {
+    for (int r = 0; r < (QR * RC8) / kThreads; ++r) {
       const int id = r * kThreads + tid;
-      const int j = id >> 5, c = id & 31;   // output row j, columns 8c .. 8c+7 (tile rows)
-      bf16_t h[8];
+      const int j = id / RC8, c = id % RC8;   // output row q0 + j, columns I*256 + 8c .. +7
+      const bool diag = diag_off >= 0 && j >= diag_off && j < diag_off + D;
+      if (j < valid_cols && !diag) {
+        bf16_t h[8];
 #pragma unroll
-      for (int e = 0; e < 8; ++e) h[e] = T[tidx(8 * c + e, j)];
-      uint4 v;
-      v.x = pack2(h[0], h[1]); v.y = pack2(h[2], h[3]);
-      v.z = pack2(h[4], h[5]); v.w = pack2(h[6], h[7]);
-      *reinterpret_cast<uint4*>(out2 + (size_t)(J * TILE + j) * ld2 + I * TILE + c * 8) = v;
+        for (int e = 0; e < 8; ++e) h[e] = T[tidx(8 * c + e, j)];
+        uint4 v;
+        v.x = pack2(h[0], h[1]); v.y = pack2(h[2], h[3]);
+        v.z = pack2(h[4], h[5]); v.w = pack2(h[6], h[7]);
+        store_nt(out2 + (size_t)(q0 + j) * ld2 + I * TILE + c * 8, v);
+      }
     }
   }
 }
@@ -357,21 +417,18 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& g, int logical, Stages
 //    contiguous range of tiles, i.e. on whole matrices (L2 reuse).
 //  * otherwise (gridDim.x = one workgroup per CU, a multiple of 8): each
 //    workgroup loops over the tiles of its XCD's contiguous range, slot s
-//    taking tiles s, s + slots, ... The slots start a quarter tile apart
-//    (slot % 4): all tiles cost the same, so in lock step every CU would
-//    reach its epilogue at once and the stores of all CUs would queue at
-//    HBM together; staggered, a quarter of the CUs store while the rest
-//    compute. Tile counts per slot differ by at most one, so the offsets
-//    mostly fill time the short slots would idle anyway.
+//    taking tiles s, s + slots, ... (one launch of resident workgroups
+//    instead of one per tile).
+// Tile order within a matrix: full tiles (row-major over the lower triangle
+// for A/B, over all rows x columns for X'), then the wide tiles of the
+// half row.
 template <int ROLE>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void ns_gemm_bf16(GemmArgs g) {
   __shared__ __attribute__((aligned(1024))) Stages lds;
   constexpr bool kSym = (ROLE != kUpdate);
-  const int tiles_m = g.m_pad / TILE;
-  const int tiles_n = kSym ? tiles_m : g.n_pad / TILE;
-  const int per_mat = kSym ? tiles_m * (tiles_m + 1) / 2 : tiles_m * tiles_n;
-  const int total = per_mat * g.count;
+  const Geom G = geom(g, kSym);
+  const int total = G.per_mat * g.count;
   int t, t_end, step;
   if ((int)gridDim.x >= total) {
     t = xcd_remap(blockIdx.x, total);
@@ -384,15 +441,25 @@ void ns_gemm_bf16(GemmArgs g) {
     t = xcd * base + (xcd < rem ? xcd : rem) + slot;
     t_end = xcd * base + (xcd < rem ? xcd : rem) + base + (xcd < rem ? 1 : 0);
     step = gridDim.x / kXcd;
-    // Quarter-tile offset in units of s_sleep(127) (about 8K cycles): the
-    // main loop costs roughly 16 cycles per unit of K, the epilogue ~8K.
-    const int K = (ROLE == kGram) ? g.n_pad : g.m_pad;
-    const int quarter = (K * 16 + 8000) / 8128;
-    for (int i = 0; i < (slot & 3) * quarter; ++i) __builtin_amdgcn_s_sleep(127);
   }
 #pragma nounroll
   for (; t < t_end; t += step) {
-    gemm_tile<ROLE>(g, t, lds);
+    const int mat = t / G.per_mat;
+    const int u = t % G.per_mat;
+    if (u < G.full) {
+      int I, J;
+      if (kSym) {   // lower triangle, row-major: row I holds I + 1 tiles
+        I = 0;
+        while ((I + 1) * (I + 2) / 2 <= u) ++I;
+        J = u - I * (I + 1) / 2;
+      } else {
+        I = u / G.tn;
+        J = u % G.tn;
+      }
+      gemm_tile<ROLE, false>(g, mat, I, J, lds);
+    } else {
+      gemm_tile<ROLE, true>(g, mat, G.F, 2 * (u - G.full), lds);
+    }
     __syncthreads();   // the epilogue's LDS reads are done before the next fills
   }
 }
@@ -419,10 +486,14 @@ hipError_t device_cu_count(int* out) {
 
 hipError_t launch_gemm_bf16(GemmRole role, const GemmArgs& g, hipStream_t s) {
   if (g.count <= 0) return hipSuccess;
-  if (g.m_pad % TILE || g.n_pad % TILE) return hipErrorInvalidValue;
+  // m is padded to 128, n to 256 (so X'^T rows and the K of Gram are whole
+  // tiles); m <= n.
+  if (g.m_pad <= 0 || g.m_pad % 128 || g.n_pad % TILE || g.m_pad > g.n_pad) return hipErrorInvalidValue;
   if (role == kUpdate && !g.xt) return hipErrorInvalidValue;
-  const int tm = g.m_pad / TILE, tn = g.n_pad / TILE;
-  const long long per = (role == kUpdate) ? (long long)tm * tn : (long long)tm * (tm + 1) / 2;
+  const long long F = g.m_pad / TILE, half = (g.m_pad % TILE) != 0;
+  const long long tn = (role == kUpdate) ? g.n_pad / TILE : F + half;
+  const long long full = (role == kUpdate) ? F * tn : F * (F + 1) / 2;
+  const long long per = full + (half ? (tn + 1) / 2 : 0);
   const long long total = per * g.count;
   if (total <= 0 || total > 0x7fffffffLL) return hipErrorInvalidValue;
   int cus = 0;

@@ -15,7 +15,8 @@ size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
 size_t round_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
 }  // namespace
 
-int pad_granularity(muon_dtype dtype) { return dtype == MUON_BF16 ? 256 : 64; }
+int pad_granularity_m(muon_dtype dtype) { return dtype == MUON_BF16 ? 128 : 64; }
+int pad_granularity_n(muon_dtype dtype) { return dtype == MUON_BF16 ? 256 : 64; }
 
 size_t dtype_size(muon_dtype dtype) { return dtype == MUON_BF16 ? 2 : 4; }
 
@@ -82,7 +83,7 @@ int build_plan(const int* rows, const int* cols, int num, muon_dtype dtype, size
     if (x.first.second != y.first.second) return x.first.second > y.first.second;
     return x.first.first > y.first.first;
   });
-  const int pg = pad_granularity(dtype);
+  const int pgm = pad_granularity_m(dtype), pgn = pad_granularity_n(dtype);
   size_t ws = 0;
   for (size_t gi = 0; gi < g.size(); ++gi) {
     const int m = g[gi].first.first, n = g[gi].first.second;
@@ -91,7 +92,7 @@ int build_plan(const int* rows, const int* cols, int num, muon_dtype dtype, size
     const size_t per_mat = (size_t)m * (size_t)n;
     size_t per_batch = std::max<size_t>(1, cap / per_mat);
     int nb = (int)((cnt + per_batch - 1) / per_batch);
-    const int m_pad = (int)round_up(m, pg), n_pad = (int)round_up(n, pg);
+    const int m_pad = (int)round_up(m, pgm), n_pad = (int)round_up(n, pgn);
     int start = 0;
     for (int b = 0; b < nb; ++b) {
       int c = cnt / nb + (b < cnt % nb ? 1 : 0);  // balanced sizes

@@ -46,10 +46,12 @@ struct Layout {
   int ew_blocks = 0;    // elementwise tiles per matrix
 };
 
-// Padding granularity of the GEMM kernels for a dtype (rows and columns of
-// the wide matrix are rounded up to it; the padding holds zeros, which the
-// NS iteration keeps at zero).
-int pad_granularity(muon_dtype dtype);
+// Padding granularity of the GEMM kernels for a dtype: the wide matrix's
+// rows (m) and columns (n) are rounded up to these (bf16: m to 128, with
+// half-height tiles covering an odd multiple; n to 256). The padding holds
+// zeros, which the NS iteration keeps at zero.
+int pad_granularity_m(muon_dtype dtype);
+int pad_granularity_n(muon_dtype dtype);
 size_t dtype_size(muon_dtype dtype);
 
 Layout batch_layout(int count, int m_pad, int n_pad, muon_dtype dtype);

@@ -28,15 +28,17 @@ int main() {
     CHECK(p.batches.size() == 3);
     CHECK(p.batches[0].count == 171 && p.batches[1].count == 171 && p.batches[2].count == 170);
     for (auto& b : p.batches) {
-      CHECK(b.m == 1408 && b.n == 2048 && b.m_pad == 1536 && b.n_pad == 2048);
+      CHECK(b.m == 1408 && b.n == 2048 && b.m_pad == 1408 && b.n_pad == 2048);  // m: 128-granular
       CHECK((size_t)b.count * 1408 * 2048 <= MUON_DEFAULT_BATCH_CAP);
     }
     CHECK(p.transposed[0] == 1 && p.transposed[300] == 0);
     CHECK(p.order.size() == 512 && p.order[0] == 0 && p.order[511] == 511);
-    Layout L = batch_layout(171, 1536, 2048, MUON_BF16);
+    Layout L = batch_layout(171, 1408, 2048, MUON_BF16);
     CHECK(L.x0 % 512 == 0 && L.x1 % 512 == 0 && L.a % 512 == 0 && L.b % 512 == 0);
+    CHECK(L.xt0 % 512 == 0 && L.xt1 % 512 == 0 && L.xt0 != L.x0 && L.xt1 != L.x1);
     CHECK(L.partials % 512 == 0 && L.scales % 512 == 0);
-    CHECK(L.ew_blocks == 24 * 32);
+    CHECK(L.ew_blocks == 22 * 32);
+    CHECK(L.total >= (size_t)171 * (4 * 1408 * 2048 + 2 * 1408 * 1408) * 2);
     CHECK(p.workspace_bytes == L.total);
   }
   // Mixed stack: groups in descending element count, balanced batches.
@@ -60,6 +62,7 @@ int main() {
     CHECK(build_plan(r, c, 3, MUON_BF16, 0, p, err) == MUON_OK);
     CHECK(p.batches.size() == 2);
     CHECK(p.batches[0].m == 130 && p.batches[0].n == 300 && p.batches[0].m_pad == 256 && p.batches[0].n_pad == 512);
+    CHECK(p.batches[1].m_pad == 128 && p.batches[1].n_pad == 256);
     CHECK(p.batches[1].m == 3 && p.batches[1].n == 5 && p.batches[1].count == 2);
     CHECK(p.order[1] == 0 && p.order[2] == 2);
     Plan q;

@@ -74,7 +74,10 @@ def test_tiny_fp32_closed_form_3x5(nsa):
 # ---- small and ragged shapes, several tiles -------------------------------
 
 RAGGED = [(200, 333), (333, 200), (128, 128), (256, 640), (1, 1), (1, 7), (7, 1), (64, 128),
-          (130, 300), (129, 1000), (300, 130), (384, 256)]
+          (130, 300), (129, 1000), (300, 130), (384, 256),
+          # short side padded to an odd multiple of 128 (half tile row), and
+          # an odd number of 256-column tiles
+          (300, 520), (600, 700), (700, 600), (384, 896)]
 
 
 @pytest.mark.parametrize("dtype,tol", [("bf16", BF16_TOL), ("f32", F32_TOL)])
