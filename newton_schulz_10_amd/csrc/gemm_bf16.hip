@@ -363,9 +363,26 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& g, int mat, int I, int
   }
   constexpr int D = WIDE ? 128 : 256;   // edge of a diagonal block
   if (diag_off >= 0) {
-    for (int idx = tid; idx < D * D; idx += kThreads) {
-      const int i = idx / D, j = idx % D;
-      if (i > j) T[tidx(i, diag_off + j)] = T[tidx(j, diag_off + i)];
+    // One 16 B chunk (row i, columns 8c .. 8c+7 of the block) per step: a
+    // chunk wholly below the diagonal is gathered from column i of the
+    // rows above and written at once; the chunk holding the diagonal is
+    // filled element by element.
+    for (int idx = tid; idx < D * (D / 8); idx += kThreads) {
+      const int i = idx / (D / 8), c = idx % (D / 8);
+      if (8 * c + 7 < i) {
+        bf16_t h[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) h[e] = T[tidx(8 * c + e, diag_off + i)];
+        uint4 v;
+        v.x = pack2(h[0], h[1]); v.y = pack2(h[2], h[3]);
+        v.z = pack2(h[4], h[5]); v.w = pack2(h[6], h[7]);
+        *reinterpret_cast<uint4*>(T + i * QR + ((((diag_off >> 3) + c) ^ eswz(i)) << 3)) = v;
+      } else if (8 * c <= i) {
+        for (int e = 0; e < 8; ++e) {
+          const int j = 8 * c + e;
+          if (j < i) T[tidx(i, diag_off + j)] = T[tidx(j, diag_off + i)];
+        }
+      }
     }
     __syncthreads();
   }
