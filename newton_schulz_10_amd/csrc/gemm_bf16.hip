@@ -55,6 +55,8 @@ namespace {
 typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8;
 typedef __attribute__((ext_vector_type(16))) float f32x16;
 typedef __attribute__((ext_vector_type(4))) unsigned u32x4;
+typedef __attribute__((ext_vector_type(4))) short s16x4;
+typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
 
 constexpr int TILE = 256;            // full tile edge
 constexpr int BK = 32;               // K per LDS stage
@@ -317,25 +319,36 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& g, int mat, int I, int
     lds_barrier();
   }
 
-  // Each wave forms its outputs in fp32 and writes bf16 into T.
+  // Each wave forms its outputs in fp32 and writes bf16 into T, one row
+  // block at a time: all 16 operand reads of the block are issued before
+  // any write (written in place, so the compiler would otherwise order
+  // every read after the previous write).
 #pragma unroll
   for (int b = 0; b < 4; ++b) {
     const int i = rb0 + b * 32 + (lane & 31);
     bf16_t* row = T + i * QR;
     const int sw = eswz(i);
+    auto at = [&](int a, int q) {
+      const int j = cb0 + a * 32 + 8 * q + 4 * (lane >> 5);
+      return reinterpret_cast<uint2*>(row + (((j >> 3) ^ sw) << 3) + (j & 7));
+    };
+    uint2 w[4][4];
+    if (ROLE == kPoly || ROLE == kUpdate) {
+#pragma unroll
+      for (int a = 0; a < 4; ++a)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) w[a][q] = *at(a, q);
+    }
 #pragma unroll
     for (int a = 0; a < 4; ++a) {
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
-        const int j = cb0 + a * 32 + 8 * q + 4 * (lane >> 5);
-        uint2* p = reinterpret_cast<uint2*>(row + (((j >> 3) ^ sw) << 3) + (j & 7));
         float v[4];
 #pragma unroll
         for (int e = 0; e < 4; ++e) v[e] = acc[a][b][4 * q + e];
         if (ROLE == kPoly || ROLE == kUpdate) {
-          const uint2 w = *p;
-          const float x[4] = {bf16_to_f32(w.x & 0xffffu), bf16_to_f32(w.x >> 16),
-                              bf16_to_f32(w.y & 0xffffu), bf16_to_f32(w.y >> 16)};
+          const float x[4] = {bf16_to_f32(w[a][q].x & 0xffffu), bf16_to_f32(w[a][q].x >> 16),
+                              bf16_to_f32(w[a][q].y & 0xffffu), bf16_to_f32(w[a][q].y >> 16)};
 #pragma unroll
           for (int e = 0; e < 4; ++e)
             v[e] = (ROLE == kPoly) ? fmaf(g.cb, x[e], g.cc * v[e]) : sc * fmaf(g.ca, x[e], v[e]);
@@ -346,7 +359,7 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& g, int mat, int I, int
         uint2 o;
         o.x = pack2(f32_to_bf16(v[0]), f32_to_bf16(v[1]));
         o.y = pack2(f32_to_bf16(v[2]), f32_to_bf16(v[3]));
-        *p = o;
+        *at(a, q) = o;
       }
     }
   }
@@ -362,27 +375,41 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& g, int mat, int I, int
     if (WIDE && (I == J || I == J + 1)) diag_off = (I - J) * TILE;
   }
   constexpr int D = WIDE ? 128 : 256;   // edge of a diagonal block
-  if (diag_off >= 0) {
-    // One 16 B chunk (row i, columns 8c .. 8c+7 of the block) per step: a
-    // chunk wholly below the diagonal is gathered from column i of the
-    // rows above and written at once; the chunk holding the diagonal is
-    // filled element by element.
-    for (int idx = tid; idx < D * (D / 8); idx += kThreads) {
-      const int i = idx / (D / 8), c = idx % (D / 8);
-      if (8 * c + 7 < i) {
-        bf16_t h[8];
+  // Transposing LDS read (ds_read_b64_tr_b16): in each 16-lane group, lane
+  // jj names 4 elements of tile row r0 + jj/4 (columns c0 + 4*(jj%4) ..)
+  // and receives the 4 elements of column c0 + jj in rows r0 .. r0+3.
+  // Group grp covers rows i0 + 8*grp .. +7 with two reads, so each lane
+  // ends with 8 consecutive rows of one column: 16 B of the transposed
+  // tile.
+  const int grp = lane >> 4, jj = lane & 15;
+  auto tr8 = [&](int i0, int c0) {
+    s16x4 h[2];
 #pragma unroll
-        for (int e = 0; e < 8; ++e) h[e] = T[tidx(8 * c + e, diag_off + i)];
-        uint4 v;
-        v.x = pack2(h[0], h[1]); v.y = pack2(h[2], h[3]);
-        v.z = pack2(h[4], h[5]); v.w = pack2(h[6], h[7]);
-        *reinterpret_cast<uint4*>(T + i * QR + ((((diag_off >> 3) + c) ^ eswz(i)) << 3)) = v;
-      } else if (8 * c <= i) {
-        for (int e = 0; e < 8; ++e) {
-          const int j = 8 * c + e;
-          if (j < i) T[tidx(i, diag_off + j)] = T[tidx(j, diag_off + i)];
-        }
-      }
+    for (int half = 0; half < 2; ++half) {
+      const int row = i0 + 8 * grp + 4 * half + (jj >> 2);
+      h[half] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(T + tidx(row, c0 + 4 * (jj & 3))));
+    }
+    return __builtin_bit_cast(uint4, __builtin_shufflevector(h[0], h[1], 0, 1, 2, 3, 4, 5, 6, 7));
+  };
+  if (diag_off >= 0) {
+    // Lower part of the block = upper part transposed. Away from the
+    // diagonal, 32-row x 16-column blocks of the upper part (rows i0 ..,
+    // columns jb .. with jb >= i0 + 32) are gathered with transposing reads
+    // and written as 16 B chunks of the lower part (rows jb + jj, columns
+    // i0 + 8*grp ..); the 32 x 32 blocks on the diagonal go element by
+    // element. Reads touch only the upper part, writes only the lower.
+    constexpr int NBLK = (D / 32) * (D / 32 - 1);   // (i0, jb) pairs with jb >= i0 + 32
+    for (int blk = wave; blk < NBLK; blk += 4) {
+      int i0 = 0, rest = blk;   // row group i0 has (D - i0 - 32) / 16 column groups
+      while (rest >= (D - i0 - 32) / 16) { rest -= (D - i0 - 32) / 16; i0 += 32; }
+      const int jb = i0 + 32 + 16 * rest;
+      const uint4 v = tr8(i0, diag_off + jb);
+      const int r = jb + jj, c = diag_off + i0 + 8 * grp;
+      *reinterpret_cast<uint4*>(T + r * QR + (((c >> 3) ^ eswz(r)) << 3)) = v;
+    }
+    for (int idx = tid; idx < D * 32; idx += kThreads) {
+      const int blk = idx >> 10, i = blk * 32 + ((idx >> 5) & 31), j = blk * 32 + (idx & 31);
+      if (i > j) T[tidx(i, diag_off + j)] = T[tidx(j, diag_off + i)];
     }
     __syncthreads();
   }
@@ -408,22 +435,16 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& g, int mat, int I, int
     out2 = static_cast<bf16_t*>(g.out2) + (size_t)mat * g.mat_x;
   }
   if (out2) {
-    constexpr int RC8 = PR / 8;   // chunks per transposed row
+    // 16 columns x 32 rows per wave step; the four groups' 16 B stores of a
+    // transposed row are contiguous (64 B).
     const int ld2 = g.m_pad;
+    constexpr int NJ = QR / 16, NI = PR / 32;   // column groups, row groups
 #pragma unroll 2
-    for (int r = 0; r < (QR * RC8) / kThreads; ++r) {
-      const int id = r * kThreads + tid;
-      const int j = id / RC8, c = id % RC8;   // output row q0 + j, columns I*256 + 8c .. +7
-      const bool diag = diag_off >= 0 && j >= diag_off && j < diag_off + D;
-      if (j < valid_cols && !diag) {
-        bf16_t h[8];
-#pragma unroll
-        for (int e = 0; e < 8; ++e) h[e] = T[tidx(8 * c + e, j)];
-        uint4 v;
-        v.x = pack2(h[0], h[1]); v.y = pack2(h[2], h[3]);
-        v.z = pack2(h[4], h[5]); v.w = pack2(h[6], h[7]);
-        store_nt(out2 + (size_t)(q0 + j) * ld2 + I * TILE + c * 8, v);
-      }
+    for (int r = wave; r < NJ * NI; r += 4) {
+      const int jb = (r / NI) * 16, i0 = (r % NI) * 32;
+      const bool diag = diag_off >= 0 && jb >= diag_off && jb < diag_off + D;
+      if (jb < valid_cols && !diag)
+        store_nt(out2 + (size_t)(q0 + jb + jj) * ld2 + I * TILE + i0 + 8 * grp, tr8(i0, jb));
     }
   }
 }
