@@ -13,10 +13,18 @@ __device__ __forceinline__ float bf16_to_f32(bf16_t h) {
   return __uint_as_float(static_cast<unsigned>(h) << 16);
 }
 
-// Round to nearest, ties to even (gfx950's v_cvt_pk_bf16_f32, which the
-// compiler pairs up for neighbouring conversions); NaN stays NaN.
+// Round to nearest, ties to even (gfx950's v_cvt_pk_bf16_f32); NaN stays
+// NaN.
 __device__ __forceinline__ bf16_t f32_to_bf16(float f) {
   return __builtin_bit_cast(bf16_t, static_cast<__bf16>(f));
+}
+
+// Two values rounded as one packed pair (lo in bits 0..15): a single
+// v_cvt_pk_bf16_f32 instead of two conversions and a repack.
+typedef __attribute__((ext_vector_type(2))) float f32x2_t;
+typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2_t;
+__device__ __forceinline__ unsigned f32x2_to_bf16x2(float lo, float hi) {
+  return __builtin_bit_cast(unsigned, __builtin_convertvector(f32x2_t{lo, hi}, bf16x2_t));
 }
 
 template <typename T> struct Elem;

@@ -49,8 +49,8 @@ __device__ __forceinline__ void store4(ST* p, int valid, const float v[4]) {
       *reinterpret_cast<float4*>(p) = make_float4(v[0], v[1], v[2], v[3]);
     } else {
       uint2 q;
-      q.x = f32_to_bf16(v[0]) | (static_cast<unsigned>(f32_to_bf16(v[1])) << 16);
-      q.y = f32_to_bf16(v[2]) | (static_cast<unsigned>(f32_to_bf16(v[3])) << 16);
+      q.x = f32x2_to_bf16x2(v[0], v[1]);
+      q.y = f32x2_to_bf16x2(v[2], v[3]);
       *reinterpret_cast<uint2*>(p) = q;
     }
   } else {

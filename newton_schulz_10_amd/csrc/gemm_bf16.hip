@@ -6,10 +6,14 @@
 // batched NS iteration, a single sequence of batched matmuls, in bf16.
 // Per NS step and matrix (X is m x n, m <= n, zero padded; X^T is kept as a
 // second n x m copy so that every product reads K-contiguous rows):
-//   Gram   : A  = sc * X X^T          rows of X  . rows of X     (K = n)
-//   Poly   : B  = b*A + c*(A A^T)     rows of A  . rows of A     (K = m)
-//   Update : X' = sc * (a*X + B X)    rows of B  . rows of X^T   (K = m)
-// A and B are symmetric: Gram and Poly compute only the tiles on or below
+//   Gram   : A  = sc * X X^T              rows of X  . rows of X    (K = n)
+//   Poly   : B' = a*I + b*A + c*(A A^T)   rows of A  . rows of A    (K = m)
+//   Update : X' = sc * (B' X)             rows of B' . rows of X^T  (K = m)
+// The page writes the step as X' = a X + B X with B = b A + c A A; here the
+// a X term is moved into the diagonal of B' (the same product, one more
+// rounding of the diagonal to bf16, relative 2^-9 of the a X term like the
+// rounding of X itself), so that Update needs no operand in its epilogue.
+// A and B' are symmetric: Gram and Poly compute only the tiles on or below
 // the diagonal and store each one twice (tile and mirror). Update stores
 // X' and X'^T. sc is the first step's Frobenius scale (s^2 for Gram, s for
 // Update) and 1 afterwards. Accumulation is fp32 on
@@ -34,10 +38,10 @@
 //  * The fill loads are interleaved with the MFMAs (one 1 KiB load after
 //    every 4 MFMAs): issued in a burst they back up the address unit and
 //    stall the wave's MFMA issue behind them.
-//  * Epilogue through LDS: the operand tile of Poly/Update is loaded into
-//    LDS with coalesced direct loads, each wave forms its outputs in fp32
+//  * Epilogue through LDS: the operand tile of Poly is loaded into LDS
+//    with coalesced direct loads, each wave forms its outputs in fp32
 //    and writes bf16 back in place, and the finished tile leaves LDS as
-//    coalesced 16 B non-temporal row stores and, transposed, as the mirror
+//    coalesced 16 B row stores and, transposed, as the mirror
 //    tile (Gram/Poly) or the X'^T tile (Update).
 //  * One grid covers every tile of every matrix of the batch: one workgroup
 //    per CU looping over a contiguous (per XCD) range of tiles, so each
@@ -99,12 +103,20 @@ __device__ __forceinline__ void dma16(const void* g, const void* lds_dst) {
 // from moving LDS accesses across it.
 __device__ __forceinline__ void lds_barrier() { asm volatile("s_barrier" ::: "memory"); }
 
-__device__ __forceinline__ unsigned pack2(bf16_t lo, bf16_t hi) {
-  return static_cast<unsigned>(lo) | (static_cast<unsigned>(hi) << 16);
+// Marks a batch of LDS reads as consumed here: the compiler can then not
+// sink each read into the (conditional) block of its store, where every
+// read would wait for its own data.
+template <int N>
+__device__ __forceinline__ void keep_batch(uint4 (&v)[N]) {
+#pragma unroll
+  for (int u = 0; u < N; ++u) asm volatile("" :: "v"(__builtin_bit_cast(u32x4, v[u])));
 }
-
-__device__ __forceinline__ void store_nt(bf16_t* p, uint4 v) {
-  __builtin_nontemporal_store(__builtin_bit_cast(u32x4, v), reinterpret_cast<u32x4*>(p));
+// 16 B store at a uniform base plus a 32-bit per-lane element offset (the
+// scalar base + vector offset addressing form: one VGPR of address per
+// store). Plain stores: with every CU storing at once they sustain more
+// bandwidth than non-temporal ones.
+__device__ __forceinline__ void store16_at(bf16_t* base, unsigned elem_off, uint4 v) {
+  *reinterpret_cast<u32x4*>(reinterpret_cast<char*>(base) + 2u * elem_off) = __builtin_bit_cast(u32x4, v);
 }
 
 // s_waitcnt immediates: vmcnt(n) with expcnt/lgkmcnt unconstrained, and
@@ -280,6 +292,15 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& g, int mat, int I, int
   slab(last, std::false_type{});
 
   // ---- epilogue ----------------------------------------------------------
+  {
+  // Thread indices of the epilogue come from a fresh opaque copy of the
+  // thread id: none of its address arithmetic can then be scheduled into
+  // the last slab, where those values would stay live across the MFMAs.
+  int etid = threadIdx.x;
+  asm volatile("" : "+v"(etid));
+  const int tid = etid, lane = etid & 63, wave = etid >> 6;
+  const int rb0 = WIDE ? 0 : (wave >> 1) * 128;
+  const int cb0 = WIDE ? wave * 128 : (wave & 1) * 128;
   // acc[a][b] element v: tile row i = rb0 + 32b + lane%32, tile columns
   // j .. j+3 with j = cb0 + 32a + 8*(v/4) + 4*(lane/32). T is the tile in
   // LDS, PR rows x QR columns, 16 B chunks swizzled by eswz(row).
@@ -298,14 +319,20 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& g, int mat, int I, int
   __builtin_amdgcn_s_waitcnt(0x0070);  // vmcnt(0) lgkmcnt(0): stages no longer read
   lds_barrier();
 
-  if (ROLE == kPoly || ROLE == kUpdate) {
-    // Epilogue operand tile (A for Poly, X for Update; both ldo wide) into
-    // T: 128 loads of 1 KiB, 32 per wave; lane l of a load takes stored
-    // chunk l % TC8 of its row, i.e. source chunk (l % TC8) ^ eswz(row).
-    const bf16_t* E = (ROLE == kPoly)
-        ? static_cast<const bf16_t*>(g.a) + (size_t)mat * g.mat_a
-        : static_cast<const bf16_t*>(g.x) + (size_t)mat * g.mat_x;
-    E += (size_t)(I * TILE) * ldo;
+  // Diagonal blocks of A/B: the full tile I == J, or the 128 x 128 corner
+  // of a wide tile (tile columns diag_off ..); tile row i meets the global
+  // diagonal at tile column i + diag_off.
+  int diag_off = -1;
+  if (kSym) {
+    if (!WIDE && I == J) diag_off = 0;
+    if (WIDE && (I == J || I == J + 1)) diag_off = (I - J) * TILE;
+  }
+
+  if (ROLE == kPoly) {
+    // Epilogue operand tile A into T: 128 loads of 1 KiB, 32 per wave; lane
+    // l of a load takes stored chunk l % TC8 of its row, i.e. source chunk
+    // (l % TC8) ^ eswz(row).
+    const bf16_t* E = static_cast<const bf16_t*>(g.a) + (size_t)mat * g.mat_a + (size_t)(I * TILE) * ldo;
     constexpr int RPI = 1024 / (QR * 2);   // tile rows per load
 #pragma unroll 8
     for (int q = 0; q < 32; ++q) {
@@ -323,6 +350,18 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& g, int mat, int I, int
   // block at a time: all 16 operand reads of the block are issued before
   // any write (written in place, so the compiler would otherwise order
   // every read after the previous write).
+  //   Gram:   A  = sc * acc
+  //   Poly:   B' = a I + b A + c acc   (a on the diagonal: DG instance)
+  //   Update: X' = sc * acc            (acc = B' X)
+  // A wave's block holds diagonal elements only if rb0 + diag_off == cb0;
+  // then they sit in acc[b][b], element 4*(l/8) + l%4 (l = lane % 32) of
+  // the lanes with lane/32 == (l/4) % 2.
+  const int l32 = lane & 31;
+  const int dsel = (diag_off >= 0 && rb0 + diag_off == cb0 && (lane >> 5) == ((l32 >> 2) & 1))
+                       ? 4 * (l32 >> 3) + (l32 & 3) : -1;
+  auto form = [&](auto dg, auto scaled) {
+    constexpr bool DG = decltype(dg)::value;
+    constexpr bool SC = decltype(scaled)::value;
 #pragma unroll
   for (int b = 0; b < 4; ++b) {
     const int i = rb0 + b * 32 + (lane & 31);
@@ -333,7 +372,7 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& g, int mat, int I, int
       return reinterpret_cast<uint2*>(row + (((j >> 3) ^ sw) << 3) + (j & 7));
     };
     uint2 w[4][4];
-    if (ROLE == kPoly || ROLE == kUpdate) {
+    if (ROLE == kPoly) {
 #pragma unroll
       for (int a = 0; a < 4; ++a)
 #pragma unroll
@@ -346,34 +385,38 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& g, int mat, int I, int
         float v[4];
 #pragma unroll
         for (int e = 0; e < 4; ++e) v[e] = acc[a][b][4 * q + e];
-        if (ROLE == kPoly || ROLE == kUpdate) {
+        if (ROLE == kPoly) {
           const float x[4] = {bf16_to_f32(w[a][q].x & 0xffffu), bf16_to_f32(w[a][q].x >> 16),
                               bf16_to_f32(w[a][q].y & 0xffffu), bf16_to_f32(w[a][q].y >> 16)};
 #pragma unroll
-          for (int e = 0; e < 4; ++e)
-            v[e] = (ROLE == kPoly) ? fmaf(g.cb, x[e], g.cc * v[e]) : sc * fmaf(g.ca, x[e], v[e]);
-        } else {
+          for (int e = 0; e < 4; ++e) v[e] = fmaf(g.cb, x[e], g.cc * v[e]);
+          if (DG && a == b) {
+#pragma unroll
+            for (int e = 0; e < 4; ++e) v[e] += (4 * q + e == dsel) ? g.ca : 0.0f;
+          }
+        } else if (SC) {
 #pragma unroll
           for (int e = 0; e < 4; ++e) v[e] *= sc;
         }
         uint2 o;
-        o.x = pack2(f32_to_bf16(v[0]), f32_to_bf16(v[1]));
-        o.y = pack2(f32_to_bf16(v[2]), f32_to_bf16(v[3]));
+        o.x = f32x2_to_bf16x2(v[0], v[1]);
+        o.y = f32x2_to_bf16x2(v[2], v[3]);
         *at(a, q) = o;
       }
     }
   }
+  };
+  if (ROLE == kPoly && diag_off >= 0)
+    form(std::true_type{}, std::false_type{});
+  else if (ROLE != kPoly && g.scales)
+    form(std::false_type{}, std::true_type{});
+  else
+    form(std::false_type{}, std::false_type{});
   __syncthreads();
 
-  // Diagonal blocks of A/B (full tile I == J, or the 128 x 128 corner of a
-  // wide tile) are made exactly symmetric: lower part = upper part
+  // Diagonal blocks are made exactly symmetric: lower part = upper part
   // transposed (reads touch only i < j, writes only i > j). They have no
   // mirror elsewhere.
-  int diag_off = -1;   // tile column of the diagonal block, if any
-  if (kSym) {
-    if (!WIDE && I == J) diag_off = 0;
-    if (WIDE && (I == J || I == J + 1)) diag_off = (I - J) * TILE;
-  }
   constexpr int D = WIDE ? 128 : 256;   // edge of a diagonal block
   // Transposing LDS read (ds_read_b64_tr_b16): in each 16-lane group, lane
   // jj names 4 elements of tile row r0 + jj/4 (columns c0 + 4*(jj%4) ..)
@@ -414,15 +457,26 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& g, int mat, int I, int
     __syncthreads();
   }
 
-  // Tile rows -> out: TC8 lanes store one row (non-temporal: the output is
-  // read by the next kernel, not this one).
-#pragma unroll 4
-  for (int r = 0; r < (PR * TC8) / kThreads; ++r) {
-    const int id = r * kThreads + tid;
-    const int i = id / TC8, c = id % TC8;
-    if (c * 8 < valid_cols) {
-      const uint4 v = *reinterpret_cast<const uint4*>(T + i * QR + ((c ^ eswz(i)) << 3));
-      store_nt(out + (size_t)(I * TILE + i) * ldo + q0 + c * 8, v);
+  // Tile rows -> out: TC8 lanes store one row. Reads go in batches of 8
+  // ahead of their stores, so the LDS latency is paid once per batch.
+  constexpr int kBatch = 8;
+  // Uniform tile base plus 32-bit per-lane offsets (scalar-base addressing).
+  bf16_t* const otile = out + (size_t)(I * TILE) * ldo + q0;
+#pragma unroll
+  for (int r0 = 0; r0 < (PR * TC8) / kThreads; r0 += kBatch) {
+    uint4 v[kBatch];
+#pragma unroll
+    for (int u = 0; u < kBatch; ++u) {
+      const int id = (r0 + u) * kThreads + tid;
+      const int i = id / TC8, c = id % TC8;
+      v[u] = *reinterpret_cast<const uint4*>(T + i * QR + ((c ^ eswz(i)) << 3));
+    }
+    keep_batch(v);
+#pragma unroll
+    for (int u = 0; u < kBatch; ++u) {
+      const int id = (r0 + u) * kThreads + tid;
+      const int i = id / TC8, c = id % TC8;
+      if (c * 8 < valid_cols) store16_at(otile, i * ldo + c * 8, v[u]);
     }
   }
 
@@ -438,14 +492,28 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& g, int mat, int I, int
     // 16 columns x 32 rows per wave step; the four groups' 16 B stores of a
     // transposed row are contiguous (64 B).
     const int ld2 = g.m_pad;
+    bf16_t* const o2tile = out2 + (size_t)q0 * ld2 + I * TILE;
     constexpr int NJ = QR / 16, NI = PR / 32;   // column groups, row groups
-#pragma unroll 2
-    for (int r = wave; r < NJ * NI; r += 4) {
-      const int jb = (r / NI) * 16, i0 = (r % NI) * 32;
-      const bool diag = diag_off >= 0 && jb >= diag_off && jb < diag_off + D;
-      if (jb < valid_cols && !diag)
-        store_nt(out2 + (size_t)(q0 + jb + jj) * ld2 + I * TILE + i0 + 8 * grp, tr8(i0, jb));
+    static_assert((NJ * NI / 4) % kBatch == 0, "whole batches per wave");
+#pragma unroll
+    for (int r0 = wave; r0 < NJ * NI; r0 += 4 * kBatch) {
+      uint4 v[kBatch];
+#pragma unroll
+      for (int u = 0; u < kBatch; ++u) {
+        const int r = r0 + 4 * u;
+        v[u] = tr8((r % NI) * 32, (r / NI) * 16);
+      }
+      keep_batch(v);
+#pragma unroll
+      for (int u = 0; u < kBatch; ++u) {
+        const int r = r0 + 4 * u;
+        const int jb = (r / NI) * 16, i0 = (r % NI) * 32;
+        const bool diag = diag_off >= 0 && jb >= diag_off && jb < diag_off + D;
+        if (jb < valid_cols && !diag)
+          store16_at(o2tile, (jb + jj) * ld2 + i0 + 8 * grp, v[u]);
+      }
     }
+  }
   }
 }
 
