@@ -224,6 +224,18 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& g, int mat, int I, int
     }
   };
 
+  // One fragment of a step: f = 0..7 in the order the step's MFMAs first
+  // use them (rf0, cf0, rf1, rf2, rf3, cf1, cf2, cf3).
+  auto read_one = [&](int kt, int ks, int f, bf16x8 (&rf)[4], bf16x8 (&cf)[4]) {
+    const bf16_t* S = lds[kt & (kStages - 1)];
+    const int ch = 2 * ks + (lane >> 5);
+    const bool is_c = (f == 1 || f >= 5);
+    const int idx = (f == 0 || f == 1) ? 0 : (f <= 4 ? f - 1 : f - 4);
+    const int r = (is_c ? PR + cb0 : rb0) + idx * 32 + (lane & 31);
+    const bf16x8 v = *reinterpret_cast<const bf16x8*>(S + r * BK + ((ch ^ kswz(r)) * 8));
+    if (is_c) cf[idx] = v; else rf[idx] = v;
+  };
+
   f32x16 acc[4][4];  // [column block][row block]
 #pragma unroll
   for (int a = 0; a < 4; ++a)
@@ -246,21 +258,24 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& g, int mat, int I, int
 
   bf16x8 rf[2][4], cf[2][4];
   read_frags(0, 0, rf[0], cf[0]);
-  // 16 MFMAs of one step; after every 4 a hook issues memory work, so
-  // loads never queue up in a burst in front of the MFMAs.
+  // 16 MFMAs of one step; after MFMA i a hook issues memory work: one
+  // fragment read of the next step after each of the first 8 and a fill
+  // load after MFMAs 1, 5, 9, 13. Issued in bursts, reads and loads queue
+  // up in front of the next MFMA and stall the wave's (in-order) issue.
   auto mfma_step = [&](int cur, auto hook) {
 #pragma unroll
     for (int a = 0; a < 4; ++a) {
 #pragma unroll
-      for (int b = 0; b < 4; ++b)
+      for (int b = 0; b < 4; ++b) {
         acc[a][b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(cf[cur][a], rf[cur][b], acc[a][b], 0, 0, 0);
-      __builtin_amdgcn_sched_barrier(0);
-      hook(a);
-      __builtin_amdgcn_sched_barrier(0);
+        __builtin_amdgcn_sched_barrier(0);
+        hook(4 * a + b);
+        __builtin_amdgcn_sched_barrier(0);
+      }
     }
   };
-  // Loads of fill half h (0: loads 0..NLh-1, 1: NLh..NL-1) issued after
-  // MFMA group a of a step.
+  // Loads of fill half h (0: loads 0..NLh-1, 1: NLh..NL-1) issued in MFMA
+  // group a of a step.
   auto fill_part = [&](int kt, int h, int a) {
 #pragma unroll
     for (int q = (a * NLh) / 4; q < ((a + 1) * NLh) / 4; ++q) fill_one(kt, h * NLh + q);
@@ -268,23 +283,28 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& g, int mat, int I, int
   // One K-slab (two 16-deep steps). `more` (compile-time) says whether a
   // next slab exists; the last slab is peeled so the loop body has no
   // data-dependent branch around LDS reads (the compiler's wait-count
-  // bookkeeping then stays exact). sched_barrier keeps the reads of the
-  // next step ahead of this step's MFMAs.
+  // bookkeeping then stays exact). Every read of a stage is issued and
+  // completed (lgkmcnt(0)) before the barrier after which that stage is
+  // filled again.
   auto slab = [&](int kt, auto more) {
-    read_frags(kt, 1, rf[1], cf[1]);
-    __builtin_amdgcn_sched_barrier(0);
     if constexpr (decltype(more)::value) {
-      mfma_step(0, [&](int a) { fill_part(kt + 3, 0, a); });
+      mfma_step(0, [&](int i) {
+        if (i < 8) read_one(kt, 1, i, rf[1], cf[1]);
+        if ((i & 3) == 1) fill_part(kt + 3, 0, i >> 2);
+      });
       // This wave's fill of slab kt+1 and its LDS reads have completed;
       // after the barrier, every wave's have, and stage (kt+3) % 4's last
       // readers (slab kt-1) are long done.
       __builtin_amdgcn_s_waitcnt(vmcnt_lgkm0(NL + NLh));
       lds_barrier();
-      read_frags(kt + 1, 0, rf[0], cf[0]);
-      __builtin_amdgcn_sched_barrier(0);
-      mfma_step(1, [&](int a) { fill_part(kt + 3, 1, a); });
+      mfma_step(1, [&](int i) {
+        if (i < 8) read_one(kt + 1, 0, i, rf[0], cf[0]);
+        if ((i & 3) == 1) fill_part(kt + 3, 1, i >> 2);
+      });
     } else {
-      mfma_step(0, [](int) {});
+      mfma_step(0, [&](int i) {
+        if (i < 8) read_one(kt, 1, i, rf[1], cf[1]);
+      });
       mfma_step(1, [](int) {});
     }
   };
