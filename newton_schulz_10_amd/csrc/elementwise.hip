@@ -81,12 +81,10 @@ __global__ __launch_bounds__(256) void momentum_kernel(EwMats mats, MomentumArgs
   const GT* g = static_cast<const GT*>(mats.src[mi]);
   float* buf = mats.buf[mi];
   XT* x0 = static_cast<XT*>(a.x0) + (size_t)(a.first + mi) * a.mat_x;
-  XT* x0t = a.x0t ? static_cast<XT*>(a.x0t) + (size_t)(a.first + mi) * a.mat_x : nullptr;
   float ss = 0.0f;
 
   if (!mats.tr[mi]) {
-    // Stored wide: element (i, j) of the m x n matrix is X0[i][j] and
-    // X0^T[j][i]; the transposed copy goes through the LDS tile.
+    // Stored wide: element (i, j) of the m x n matrix is X0[i][j].
 #pragma unroll
     for (int p = 0; p < 4; ++p) {
       const int i = ti * T + ty + 16 * p;
@@ -107,24 +105,11 @@ __global__ __launch_bounds__(256) void momentum_kernel(EwMats mats, MomentumArgs
         if (a.has_buf) store4<float>(buf + (size_t)i * a.n + j, valid, bv);
       }
       store4<XT>(x0 + (size_t)i * a.n_pad + j, 4, u);
-#pragma unroll
-      for (int e = 0; e < 4; ++e) tile[ty + 16 * p][tx * 4 + e] = u[e];
-    }
-    if (x0t) {
-      __syncthreads();
-#pragma unroll
-      for (int p = 0; p < 4; ++p) {
-        const int jl = ty + 16 * p, il = tx * 4;
-        float v[4];
-#pragma unroll
-        for (int e = 0; e < 4; ++e) v[e] = tile[il + e][jl];
-        store4<XT>(x0t + (size_t)(tj * T + jl) * a.m_pad + ti * T + il, 4, v);
-      }
     }
   } else {
-    // Stored tall: the original is n x m (rows = wide n, cols = wide m),
-    // X0[i][j] = u[j][i] and X0^T is the original layout. Read a 64x64
-    // original tile coalesced, write X0^T directly and X0 through LDS.
+    // Stored tall: the original is n x m (rows = wide n, cols = wide m) and
+    // X0[i][j] = u[j][i]. Read a 64x64 original tile coalesced and write X0
+    // through the LDS tile.
 #pragma unroll
     for (int p = 0; p < 4; ++p) {
       const int r = tj * T + ty + 16 * p;   // original row  = wide column
@@ -144,7 +129,6 @@ __global__ __launch_bounds__(256) void momentum_kernel(EwMats mats, MomentumArgs
         }
         if (a.has_buf) store4<float>(buf + (size_t)r * a.m + c, valid, bv);
       }
-      if (x0t) store4<XT>(x0t + (size_t)r * a.m_pad + c, 4, u);
 #pragma unroll
       for (int e = 0; e < 4; ++e) tile[ty + 16 * p][tx * 4 + e] = u[e];
     }

@@ -32,7 +32,6 @@ struct MomentumArgs {
   int ew_blocks;            // tiles per matrix
   int first;                // index of the chunk's first matrix in the batch
   void* x0;                 // workspace X0 of the batch
-  void* x0t;                // workspace X0^T of the batch (n_pad x m_pad), or nullptr
   size_t mat_x;             // elements per padded matrix
   float* partials;          // [batch matrices][ew_blocks]
   int has_buf;              // 0: NS input is src itself (orthogonalize)
@@ -75,12 +74,10 @@ enum GemmRole {
 };
 
 struct GemmArgs {
-  const void* x;      // X (Gram operand, Update epilogue)
-  const void* xt;     // X^T, n_pad x m_pad (bf16 Update operand)
+  const void* x;      // X (Gram and Update operand)
   const void* a;      // A (Poly operand and epilogue)
   const void* b;      // B (Update operand)
   void* out;          // output matrices
-  void* out2;         // bf16 Update: X'^T output (nullptr: not needed)
   size_t mat_x;       // elements per padded X (m_pad * n_pad)
   size_t mat_a;       // elements per padded A or B (m_pad * m_pad)
   int count;          // matrices in the batch

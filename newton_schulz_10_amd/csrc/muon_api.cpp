@@ -166,8 +166,6 @@ int run(const std::vector<MatRef>& mats, float lr, float beta, int ns_steps, muo
     const Layout L = batch_layout(B.count, B.m_pad, B.n_pad, dtype);
     void* x0 = W + L.x0;
     void* x1 = W + L.x1;
-    void* xt0 = W + L.xt0;
-    void* xt1 = W + L.xt1;
     void* Am = W + L.a;
     void* Bm = W + L.b;
     float* partials = reinterpret_cast<float*>(W + L.partials);
@@ -187,10 +185,10 @@ int run(const std::vector<MatRef>& mats, float lr, float beta, int ns_steps, muo
       }
       MomentumArgs a;
       a.count = cn; a.m = B.m; a.n = B.n; a.m_pad = B.m_pad; a.n_pad = B.n_pad;
-      a.ew_blocks = L.ew_blocks; a.first = c0; a.x0 = x0; a.x0t = bf16 ? xt0 : nullptr; a.mat_x = L.mat_x;
+      a.ew_blocks = L.ew_blocks; a.first = c0; a.x0 = x0; a.mat_x = L.mat_x;
       a.partials = partials; a.has_buf = orthogonalize_only ? 0 : 1;
       a.beta = beta; a.kg = kg; a.nesterov = o.nesterov;
-      const double bytes = cn * elems * ((orthogonalize_only ? es : es + 4 + 4) + (bf16 ? 2 * es : es));
+      const double bytes = cn * elems * ((orthogonalize_only ? es : es + 4 + 4) + es);
       ProfScope ps("momentum", 0.0, bytes, stream);
       e = launch_momentum(em, a, bf16, bf16, stream);
       if (e != hipSuccess) status = hip_fail(e, "momentum kernel launch");
@@ -208,8 +206,6 @@ int run(const std::vector<MatRef>& mats, float lr, float beta, int ns_steps, muo
     // 3. NS iterations; the Frobenius scale is folded into the first step.
     void* X = x0;
     void* Xn = x1;
-    void* XT = xt0;
-    void* XTn = xt1;
     for (int k = 0; k < ns_steps && status == MUON_OK; ++k) {
       GemmArgs g;
       g.mat_x = L.mat_x; g.mat_a = L.mat_a; g.count = B.count;
@@ -220,17 +216,14 @@ int run(const std::vector<MatRef>& mats, float lr, float beta, int ns_steps, muo
       const GemmRole roles[3] = {kGram, kPoly, kUpdate};
       const char* names[3] = {"ns_gram", "ns_poly", "ns_update"};
       for (int r = 0; r < 3; ++r) {
-        g.x = X; g.xt = XT; g.a = Am; g.b = Bm;
+        g.x = X; g.a = Am; g.b = Bm;
         g.out = r == 0 ? Am : (r == 1 ? Bm : Xn);
-        // X'^T feeds the next step's Update only.
-        g.out2 = (r == 2 && bf16 && k + 1 < ns_steps) ? XTn : nullptr;
         g.scales = (k == 0 && r != 1) ? scales : nullptr;
         ProfScope ps(names[r], gemm_flops(roles[r], g), 0.0, stream);
         e = bf16 ? launch_gemm_bf16(roles[r], g, stream) : launch_gemm_f32(roles[r], g, stream);
         if (e != hipSuccess) { status = hip_fail(e, names[r]); break; }
       }
       std::swap(X, Xn);
-      std::swap(XT, XTn);
     }
     if (status) break;
 

@@ -30,13 +30,6 @@ Layout batch_layout(int count, int m_pad, int n_pad, muon_dtype dtype) {
   size_t off = 0;
   L.x0 = off;       off = align_up(off + (size_t)count * L.mat_x * es, A);
   L.x1 = off;       off = align_up(off + (size_t)count * L.mat_x * es, A);
-  if (dtype == MUON_BF16) {
-    L.xt0 = off;    off = align_up(off + (size_t)count * L.mat_x * es, A);
-    L.xt1 = off;    off = align_up(off + (size_t)count * L.mat_x * es, A);
-  } else {
-    L.xt0 = L.x0;
-    L.xt1 = L.x1;
-  }
   L.a = off;        off = align_up(off + (size_t)count * L.mat_a * es, A);
   L.b = off;        off = align_up(off + (size_t)count * L.mat_a * es, A);
   L.partials = off; off = align_up(off + (size_t)count * (size_t)L.ew_blocks * sizeof(float), A);

@@ -37,10 +37,8 @@ struct Plan {
 };
 
 // Byte offsets of one batch's workspace regions (each 512-byte aligned).
-// bf16 batches also keep X^T (n_pad x m_pad) next to each X, so that every
-// NS product reads K-contiguous rows; xt0/xt1 equal x0/x1 (unused) for fp32.
 struct Layout {
-  size_t x0 = 0, x1 = 0, xt0 = 0, xt1 = 0, a = 0, b = 0, partials = 0, scales = 0, total = 0;
+  size_t x0 = 0, x1 = 0, a = 0, b = 0, partials = 0, scales = 0, total = 0;
   size_t mat_x = 0;     // elements per padded m_pad x n_pad matrix
   size_t mat_a = 0;     // elements per padded m_pad x m_pad matrix
   int ew_blocks = 0;    // elementwise tiles per matrix
