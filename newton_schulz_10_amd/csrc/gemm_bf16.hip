@@ -76,11 +76,11 @@ constexpr int kThreads = 256;
 __device__ __forceinline__ int kswz(int r) { return ((r >> 1) & 3) ^ ((r >> 2) & 3); }
 
 // Chunk swizzle of Update's X stage ([32 k][QR n] rows of QR*2 bytes): chunk
-// index XOR {0, 6, 10, 12}[k % 4]. A transposing fragment read touches 4
-// consecutive k rows per 16 lanes (a 32 B pair of chunks each) and per 32
-// lanes (4 chunks each); the XOR puts them on distinct banks whether the
-// LDS serves 16 lanes over 128 B or 32 lanes over 256 B per cycle.
-__device__ __forceinline__ int xswz(int k) { return ((k & 1) * 6) ^ (((k >> 1) & 1) * 10); }
+// index XOR 4*(k % 4), i.e. the 4 consecutive k rows that a transposing
+// fragment read touches sit 64 B apart. Measured per CU with the fragment
+// read pattern: 62 B/clk (the transposing read's ceiling is about 60),
+// against 58 unswizzled and 37 for XOR patterns that separate 32 B pairs.
+__device__ __forceinline__ int xswz(int k) { return (k & 3) * 4; }
 
 // Chunk swizzle of the epilogue tile (rows of 32 or 64 chunks of 16 B; the
 // XOR touches the low 5 bits only): 32 consecutive rows get 32 distinct
@@ -187,23 +187,28 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& g, int mat, int I, int
   // values would stay live across the main loop and spill).
   int tid = threadIdx.x;
   asm volatile("" : "+v"(tid));
-  const int lane = tid & 63, wave = tid >> 6;
+  // The wave index is uniform: kept in a scalar register, so the per-wave
+  // LDS addresses and fill choices below are scalar too.
+  const int lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   // Wave's 128-row block (stage rows of P) and 128-column block (of Q).
   const int rb0 = WIDE ? 0 : (wave >> 1) * 128;
   const int cb0 = WIDE ? wave * 128 : (wave & 1) * 128;
 
-  // LDS fill of one K-slab: wave w moves stage rows (of 64 B) [w*RW,
-  // (w+1)*RW) in loads of 16 rows (1 KiB); fill_one(kt, q) issues load q.
-  // Stage rows below PR are P rows ([row][32 k]). The rest hold Q: rows of
-  // Q ([row][32 k]) for Gram/Poly; for Update the slab of X itself,
+  // LDS fill of one K-slab in loads of 16 stage rows of 64 B (1 KiB); the
+  // loads are dealt round-robin over the waves (wave w issues loads w,
+  // w+4, ..., fill_one(kt, q) its q-th), so every wave moves the same mix of
+  // P and Q rows and none of them waits longer at the slab barrier. Stage
+  // rows below PR are P rows ([row][32 k]). The rest hold Q: rows of Q
+  // ([row][32 k]) for Gram/Poly; for Update the slab of X itself,
   // [32 k][QR n] (k rows of QR*2 bytes, chunks swizzled by xswz).
   const int nk = K / BK;
   const int last = nk - 1;
+  static_assert(PR % 64 == 0, "P rows take whole rounds of the four waves' loads");
   auto fill_one = [&](int kt, int q) {
     const int k0 = (kt < last ? kt : last) * BK;   // past the end: repeat the last slab
-    const int rb = wave * RW + q * 16;
+    const int rb = (q * 4 + wave) * 16;
     const bf16_t* src;
-    if (rb < PR) {
+    if (q < PR / 64) {   // rb < PR, decided at compile time
       const int r = rb + (lane >> 2);
       src = P + (size_t)r * K + k0 + ((lane & 3) ^ kswz(r)) * 8;
     } else if (ROLE == kUpdate) {
