@@ -466,9 +466,10 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& g, int mat, int I, int
     form(std::false_type{}, std::false_type{});
   __syncthreads();
 
-  // Diagonal blocks are made exactly symmetric: lower part = upper part
-  // transposed (reads touch only i < j, writes only i > j). They have no
-  // mirror elsewhere.
+  // A diagonal block needs no symmetrizing: element (i, j) and (j, i) are
+  // the same products (the MFMA multiplies exactly; a*b = b*a) summed in the
+  // same k order, with the same epilogue arithmetic, so the block comes out
+  // exactly symmetric as computed. It has no mirror elsewhere.
   constexpr int D = WIDE ? 128 : 256;   // edge of a diagonal block
   // Transposing LDS read (ds_read_b64_tr_b16): in each 16-lane group, lane
   // jj names 4 elements of tile row r0 + jj/4 (columns c0 + 4*(jj%4) ..)
@@ -486,29 +487,6 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& g, int mat, int I, int
     }
     return __builtin_bit_cast(uint4, __builtin_shufflevector(h[0], h[1], 0, 1, 2, 3, 4, 5, 6, 7));
   };
-  if (diag_off >= 0) {
-    // Lower part of the block = upper part transposed. Away from the
-    // diagonal, 32-row x 16-column blocks of the upper part (rows i0 ..,
-    // columns jb .. with jb >= i0 + 32) are gathered with transposing reads
-    // and written as 16 B chunks of the lower part (rows jb + jj, columns
-    // i0 + 8*grp ..); the 32 x 32 blocks on the diagonal go element by
-    // element. Reads touch only the upper part, writes only the lower.
-    constexpr int NBLK = (D / 32) * (D / 32 - 1);   // (i0, jb) pairs with jb >= i0 + 32
-    for (int blk = wave; blk < NBLK; blk += 4) {
-      int i0 = 0, rest = blk;   // row group i0 has (D - i0 - 32) / 16 column groups
-      while (rest >= (D - i0 - 32) / 16) { rest -= (D - i0 - 32) / 16; i0 += 32; }
-      const int jb = i0 + 32 + 16 * rest;
-      const uint4 v = tr8(i0, diag_off + jb);
-      const int r = jb + jj, c = diag_off + i0 + 8 * grp;
-      *reinterpret_cast<uint4*>(T + r * QR + (((c >> 3) ^ eswz(r)) << 3)) = v;
-    }
-    for (int idx = tid; idx < D * 32; idx += kThreads) {
-      const int blk = idx >> 10, i = blk * 32 + ((idx >> 5) & 31), j = blk * 32 + (idx & 31);
-      if (i > j) T[tidx(i, diag_off + j)] = T[tidx(j, diag_off + i)];
-    }
-    __syncthreads();
-  }
-
   // Tile rows -> out: TC8 lanes store one row. Reads go in batches of 8
   // ahead of their stores, so the LDS latency is paid once per batch.
   constexpr int kBatch = 8;

@@ -66,11 +66,14 @@ struct ApplyArgs {
 
 // Batched NS GEMM roles. All operate on padded wide matrices of a batch,
 // element strides per matrix given below. Symmetric roles compute only the
-// tiles that meet the upper triangle and mirror them.
+// tiles on one side of the diagonal and mirror them.
+//   fp32 kernels: Poly writes B = b*A + c*(A A), Update X' = sc*(a*X + B X).
+//   bf16 kernels: Poly writes B' = a*I + b*A + c*(A A), Update X' = sc*(B' X)
+//                 (the same product, with a*X moved into B').
 enum GemmRole {
   kGram = 0,    // A   = sc * X X^T                (sc = s_i^2 or 1)
-  kPoly = 1,    // B   = b*A + c*(A A)             (A symmetric)
-  kUpdate = 2   // X'  = sc * (a*X + B X)          (sc = s_i or 1)
+  kPoly = 1,    // B   (A symmetric)
+  kUpdate = 2   // X'                              (sc = s_i or 1)
 };
 
 struct GemmArgs {
