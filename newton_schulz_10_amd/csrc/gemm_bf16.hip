@@ -291,9 +291,10 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& g, int mat, int I, int
   bf16x8 rf[2][4], cf[2][4];
   read_frags(0, 0, rf[0], cf[0]);
   // 16 MFMAs of one step; after MFMA i a hook issues memory work: one
-  // fragment read of the next step after each of the first 8 and a fill
-  // load after MFMAs 1, 5, 9, 13. Issued in bursts, reads and loads queue
-  // up in front of the next MFMA and stall the wave's (in-order) issue.
+  // fragment read of the next step after each of the first 8, and the
+  // step's NLh fill loads spread over MFMAs 8..15, so no MFMA carries more
+  // than one of them. Issued in bursts, reads and loads queue up in front
+  // of the next MFMA and stall the wave's (in-order) issue.
   auto mfma_step = [&](int cur, auto hook) {
 #pragma unroll
     for (int a = 0; a < 4; ++a) {
@@ -306,11 +307,12 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& g, int mat, int I, int
       }
     }
   };
-  // Loads of fill half h (0: loads 0..NLh-1, 1: NLh..NL-1) issued in MFMA
-  // group a of a step.
-  auto fill_part = [&](int kt, int h, int a) {
+  // Loads of fill half h (0: loads 0..NLh-1, 1: NLh..NL-1) issued after
+  // MFMA i of a step: load q goes after MFMA 8 + 8q/NLh.
+  auto fill_slot = [&](int kt, int h, int i) {
 #pragma unroll
-    for (int q = (a * NLh) / 4; q < ((a + 1) * NLh) / 4; ++q) fill_one(kt, h * NLh + q);
+    for (int q = 0; q < NLh; ++q)
+      if (8 + (8 * q) / NLh == i) fill_one(kt, h * NLh + q);
   };
   // One K-slab (two 16-deep steps). `more` (compile-time) says whether a
   // next slab exists; the last slab is peeled so the loop body has no
@@ -322,7 +324,7 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& g, int mat, int I, int
     if constexpr (decltype(more)::value) {
       mfma_step(0, [&](int i) {
         if (i < 8) read_one(kt, 1, i, rf[1], cf[1]);
-        if ((i & 3) == 1) fill_part(kt + 3, 0, i >> 2);
+        fill_slot(kt + 3, 0, i);
       });
       // This wave's fill of slab kt+1 and its LDS reads have completed;
       // after the barrier, every wave's have, and stage (kt+3) % 4's last
@@ -331,7 +333,7 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& g, int mat, int I, int
       lds_barrier();
       mfma_step(1, [&](int i) {
         if (i < 8) read_one(kt + 1, 0, i, rf[0], cf[0]);
-        if ((i & 3) == 1) fill_part(kt + 3, 1, i >> 2);
+        fill_slot(kt + 3, 1, i);
       });
     } else {
       mfma_step(0, [&](int i) {
