@@ -103,6 +103,12 @@ typedef struct muon_options {
   size_t batch_cap_elems; /* max sum of rows*cols per fused batch; 0 => 2^29
                              (section 6.6: memory-safe batching). A matrix larger
                              than the cap runs in a batch of its own.            */
+  int compute_units;      /* bf16: the balanced split of a shape group into
+                             batches (same batch count or a few more, never over
+                             the cap) is chosen so that the GEMM tiles fill whole
+                             rounds of this many compute units. -1 (default): the
+                             current device's count (no fitting when no device
+                             is visible); 0: no fitting (fewest batches).      */
 } muon_options;
 
 /* Fills *opts with the defaults above. */

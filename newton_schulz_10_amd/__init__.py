@@ -38,7 +38,8 @@ class Options(ctypes.Structure):
     _fields_ = [("nesterov", ctypes.c_int), ("momentum_form", ctypes.c_int),
                 ("weight_decay", ctypes.c_float), ("scale_rule", ctypes.c_int),
                 ("rms_target", ctypes.c_float), ("eps", ctypes.c_float),
-                ("coeffs", ctypes.POINTER(ctypes.c_float)), ("batch_cap_elems", ctypes.c_size_t)]
+                ("coeffs", ctypes.POINTER(ctypes.c_float)), ("batch_cap_elems", ctypes.c_size_t),
+                ("compute_units", ctypes.c_int)]
 
 
 class Matrix(ctypes.Structure):
@@ -134,7 +135,7 @@ def _matrices(t: torch.Tensor, what: str) -> List[Tuple[int, int, int]]:
 
 
 def _options(nesterov=True, momentum_form="ema", weight_decay=0.0, scale_rule="rms", rms_target=0.2,
-             eps=1e-7, coeffs=None, batch_cap_elems=0, ns_steps=5):
+             eps=1e-7, coeffs=None, batch_cap_elems=0, compute_units=-1, ns_steps=5):
     o = Options()
     load().muon_default_options(ctypes.byref(o))
     o.nesterov = 1 if nesterov else 0
@@ -151,6 +152,7 @@ def _options(nesterov=True, momentum_form="ema", weight_decay=0.0, scale_rule="r
         keep = (ctypes.c_float * len(flat))(*flat)
         o.coeffs = ctypes.cast(keep, ctypes.POINTER(ctypes.c_float))
     o.batch_cap_elems = batch_cap_elems
+    o.compute_units = compute_units
     return o, keep
 
 
@@ -188,7 +190,7 @@ def muon_step(mats: Iterable[Tuple[torch.Tensor, torch.Tensor, torch.Tensor]], l
               beta: float = 0.95, ns_steps: int = 5, stream=None, **options) -> None:
     """C `muon_step`: one Muon step over (param, grad, momentum) triples of
     any shapes; options as in muon_options (nesterov, momentum_form,
-    weight_decay, scale_rule, rms_target, eps, coeffs, batch_cap_elems)."""
+    weight_decay, scale_rule, rms_target, eps, coeffs, batch_cap_elems, compute_units)."""
     rows = []
     dt = None
     for (p, g, m) in mats:
@@ -213,7 +215,8 @@ def muon_step(mats: Iterable[Tuple[torch.Tensor, torch.Tensor, torch.Tensor]], l
 
 
 def muon_orthogonalize(inputs: Sequence[torch.Tensor], outputs: Sequence[torch.Tensor], ns_steps: int = 5,
-                       stream=None, eps: float = 1e-7, coeffs=None, batch_cap_elems: int = 0) -> None:
+                       stream=None, eps: float = 1e-7, coeffs=None, batch_cap_elems: int = 0,
+                       compute_units: int = -1) -> None:
     """C `muon_orthogonalize`: outputs[i] = NS(inputs[i]) (same shapes)."""
     I = [x for t in inputs for x in _matrices(t, "inputs")]
     O = [x for t in outputs for x in _matrices(t, "outputs")]
@@ -225,7 +228,8 @@ def muon_orthogonalize(inputs: Sequence[torch.Tensor], outputs: Sequence[torch.T
     if any((r, c) != (m, n) for _, r, c in I + O):
         raise ValueError("all matrices must share one shape")
     dt = _dtype(inputs[0])
-    o, keep = _options(eps=eps, coeffs=coeffs, batch_cap_elems=batch_cap_elems, ns_steps=ns_steps)
+    o, keep = _options(eps=eps, coeffs=coeffs, batch_cap_elems=batch_cap_elems, compute_units=compute_units,
+                       ns_steps=ns_steps)
     arr = ctypes.c_void_p * len(I)
     _check(load().muon_orthogonalize(arr(*[p for p, _, _ in I]), arr(*[p for p, _, _ in O]), len(I), m, n,
                                      ns_steps, dt, ctypes.byref(o), _stream(stream)))
@@ -233,13 +237,13 @@ def muon_orthogonalize(inputs: Sequence[torch.Tensor], outputs: Sequence[torch.T
 
 
 def plan_query(shapes: Sequence[Tuple[int, int]], dtype: torch.dtype = torch.bfloat16,
-               batch_cap_elems: int = 0) -> dict:
+               batch_cap_elems: int = 0, compute_units: int = -1) -> dict:
     """C `muon_plan_query` (host only): the batches and order muon_step would use."""
     L = load()
     n = len(shapes)
     rows = (ctypes.c_int * max(n, 1))(*[r for r, _ in shapes])
     cols = (ctypes.c_int * max(n, 1))(*[c for _, c in shapes])
-    o, _ = _options(batch_cap_elems=batch_cap_elems)
+    o, _ = _options(batch_cap_elems=batch_cap_elems, compute_units=compute_units)
     nb = ctypes.c_int(0)
     ws = ctypes.c_size_t(0)
     _check(L.muon_plan_query(rows, cols, n, _DTYPES[dtype], ctypes.byref(o), None, 0, ctypes.byref(nb), None,

@@ -128,6 +128,19 @@ double update_scale(const muon_options& o, int rows, int cols) {
   }
 }
 
+// Compute units the batch split is fitted to: options.compute_units, or
+// for -1 the current device's count (0, i.e. no fitting, when no device is
+// visible).
+int fit_units(const muon_options& o) {
+  if (o.compute_units >= 0) return o.compute_units;
+  int dev = 0, n = 0;
+  if (hipGetDevice(&dev) != hipSuccess || hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) {
+    (void)hipGetLastError();
+    return 0;
+  }
+  return n;
+}
+
 int run(const std::vector<MatRef>& mats, float lr, float beta, int ns_steps, muon_dtype dtype,
         const muon_options& o, bool orthogonalize_only, hipStream_t stream) {
   if (mats.empty()) return MUON_OK;
@@ -136,7 +149,7 @@ int run(const std::vector<MatRef>& mats, float lr, float beta, int ns_steps, muo
   for (int i = 0; i < num; ++i) { rows[i] = mats[i].rows; cols[i] = mats[i].cols; }
   Plan plan;
   std::string err;
-  int rc = build_plan(rows.data(), cols.data(), num, dtype, o.batch_cap_elems, plan, err);
+  int rc = build_plan(rows.data(), cols.data(), num, dtype, o.batch_cap_elems, fit_units(o), plan, err);
   if (rc) return fail(rc, err);
 
   if (const char* f = std::getenv("MUON_TEST_FAIL_ALLOC"))
@@ -396,7 +409,8 @@ int muon_plan_query(const int* rows, const int* cols, int num, muon_dtype dtype,
     if (opts) o = *opts;
     Plan plan;
     std::string err;
-    int rc = build_plan(rows, cols, num, dtype, o.batch_cap_elems, plan, err);
+    if (o.compute_units < -1) return fail(MUON_ERR_INVALID_ARGUMENT, "options.compute_units must be >= -1");
+    int rc = build_plan(rows, cols, num, dtype, o.batch_cap_elems, fit_units(o), plan, err);
     if (rc) return fail(rc, err);
     if (cap > 0 && !batches) return fail(MUON_ERR_INVALID_ARGUMENT, "batches is NULL with cap > 0");
     for (int i = 0; i < cap && i < (int)plan.batches.size(); ++i) {

@@ -50,7 +50,30 @@ int check_shape(int m, int n, std::string& err, int index) {
   return MUON_OK;
 }
 
-int build_plan(const int* rows, const int* cols, int num, muon_dtype dtype, size_t cap,
+// Estimated time of the three NS GEMMs of one bf16 batch of c matrices on
+// `cus` compute units, in units of one K element of one tile. It follows the
+// bf16 GEMM's geometry: 256 x 256 tiles plus, when m_pad = 256 F + 128, wide
+// 128 x 512 tiles for the half row; Gram and Poly over the lower triangle.
+// Tiles are split into 8 equal per-XCD ranges, each worked in rounds by
+// cus/8 workgroups; a tile costs its K plus an epilogue/prologue allowance,
+// a launch a quarter of that.
+static double ns_batch_cost(long long c, int m_pad, int n_pad, int cus) {
+  const long long F = m_pad / 256, half = (m_pad % 256) != 0;
+  const long long slots = (long long)(cus / 8) * 8;
+  auto rounds = [&](long long tiles) -> long long {
+    if (slots < 8 || tiles <= slots) return 1;
+    const long long per_xcd = (tiles + 7) / 8;
+    return (per_xcd + slots / 8 - 1) / (slots / 8);
+  };
+  const long long ts = F + half, tu = n_pad / 256;
+  const long long sym = (F * (F + 1) / 2 + (half ? (ts + 1) / 2 : 0)) * c;
+  const long long upd = (F * tu + (half ? (tu + 1) / 2 : 0)) * c;
+  const double E = 640.0;   // epilogue + prologue of a tile, in K elements
+  const double L = 256.0;   // one launch
+  return rounds(sym) * (n_pad + E) + rounds(sym) * (m_pad + E) + rounds(upd) * (m_pad + E) + 3 * L;
+}
+
+int build_plan(const int* rows, const int* cols, int num, muon_dtype dtype, size_t cap, int cus,
                Plan& out, std::string& err) {
   out = Plan();
   if (num < 0) { err = "num < 0"; return MUON_ERR_INVALID_ARGUMENT; }
@@ -86,6 +109,18 @@ int build_plan(const int* rows, const int* cols, int num, muon_dtype dtype, size
     size_t per_batch = std::max<size_t>(1, cap / per_mat);
     int nb = (int)((cnt + per_batch - 1) / per_batch);
     const int m_pad = (int)round_up(m, pgm), n_pad = (int)round_up(n, pgn);
+    if (dtype == MUON_BF16 && cus > 0 && cnt > 1) {
+      // Up to four more batches than needed, if their tiles fill the
+      // compute units' rounds better (balanced sizes, as below).
+      double best = 0.0;
+      int best_nb = nb;
+      for (int t = nb; t <= std::min(cnt, nb + 4); ++t) {
+        double cost = 0.0;
+        for (int b = 0; b < t; ++b) cost += ns_batch_cost(cnt / t + (b < cnt % t ? 1 : 0), m_pad, n_pad, cus);
+        if (t == nb || cost < best) { best = cost; best_nb = t; }
+      }
+      nb = best_nb;
+    }
     int start = 0;
     for (int b = 0; b < nb; ++b) {
       int c = cnt / nb + (b < cnt % nb ? 1 : 0);  // balanced sizes
@@ -109,6 +144,7 @@ void default_options(muon_options& o) {
   o.eps = 1e-7f;
   o.coeffs = nullptr;
   o.batch_cap_elems = MUON_DEFAULT_BATCH_CAP;
+  o.compute_units = -1;
 }
 
 int check_options(const muon_options& o, int ns_steps, std::string& err) {
@@ -118,6 +154,7 @@ int check_options(const muon_options& o, int ns_steps, std::string& err) {
   if (!std::isfinite(o.weight_decay)) { err = "options.weight_decay is not finite"; return MUON_ERR_INVALID_ARGUMENT; }
   if (!std::isfinite(o.rms_target)) { err = "options.rms_target is not finite"; return MUON_ERR_INVALID_ARGUMENT; }
   if (!(o.eps >= 0.0f) || !std::isfinite(o.eps)) { err = "options.eps must be finite and >= 0"; return MUON_ERR_INVALID_ARGUMENT; }
+  if (o.compute_units < -1) { err = "options.compute_units must be >= -1"; return MUON_ERR_INVALID_ARGUMENT; }
   if (o.coeffs) {
     for (int i = 0; i < 3 * ns_steps; ++i)
       if (!std::isfinite(o.coeffs[i])) {

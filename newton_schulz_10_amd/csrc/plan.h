@@ -55,9 +55,11 @@ size_t dtype_size(muon_dtype dtype);
 Layout batch_layout(int count, int m_pad, int n_pad, muon_dtype dtype);
 
 // Groups matrices by {min, max}, orders groups by descending rows*cols,
-// splits each group into balanced batches of at most `cap` elements.
+// splits each group into balanced batches of at most `cap` elements. With
+// cus > 0 (bf16), the number of batches is the one, among the fewest and a
+// few more, whose GEMM tiles best fill whole rounds of `cus` compute units.
 // Returns MUON_OK or MUON_ERR_INVALID_ARGUMENT with `err` set.
-int build_plan(const int* rows, const int* cols, int num, muon_dtype dtype, size_t cap,
+int build_plan(const int* rows, const int* cols, int num, muon_dtype dtype, size_t cap, int cus,
                Plan& out, std::string& err);
 
 // Option defaults and validation.

@@ -79,24 +79,33 @@ def test_plan_query_moe_bank(lib):
     import torch
     import newton_schulz_10_amd as nsa
     shapes = [(2048, 1408)] * 256 + [(1408, 2048)] * 256
-    plan = nsa.plan_query(shapes, torch.bfloat16)
+    plan = nsa.plan_query(shapes, torch.bfloat16, compute_units=0)   # fewest batches
     assert [b["count"] for b in plan["batches"]] == [171, 171, 170]
     assert all(b["m"] == 1408 and b["n"] == 2048 for b in plan["batches"])
     assert plan["order"] == list(range(512))
     assert plan["workspace_bytes"] > 171 * 1408 * 2048 * 2 * 2
+    # Fitted to 256 compute units: 128 matrices give 18*128 = 9*256 Gram/Poly
+    # tiles and 44*128 = 22*256 Update tiles, whole rounds.
+    fitted = nsa.plan_query(shapes, torch.bfloat16, compute_units=256)
+    assert [b["count"] for b in fitted["batches"]] == [128] * 4
+    assert fitted["order"] == list(range(512))
+    with pytest.raises(nsa.MuonError):
+        nsa.plan_query(shapes, torch.bfloat16, compute_units=-2)
 
 
 def test_plan_query_mlp_and_stack(lib):
     import torch
     import newton_schulz_10_amd as nsa
-    mlp = nsa.plan_query([(4096, 14336)] * 32 + [(14336, 4096)] * 32, torch.bfloat16)
+    mlp = nsa.plan_query([(4096, 14336)] * 32 + [(14336, 4096)] * 32, torch.bfloat16, compute_units=0)
     assert [b["count"] for b in mlp["batches"]] == [8] * 8
-    stack = nsa.plan_query([(7168, 7168)] * 4 + [(7168, 18432)] * 2 + [(7168, 2048)] * 128, torch.bfloat16)
+    stack = nsa.plan_query([(7168, 7168)] * 4 + [(7168, 18432)] * 2 + [(7168, 2048)] * 128, torch.bfloat16,
+                           compute_units=0)
     assert [(b["m"], b["n"], b["count"]) for b in stack["batches"]] == \
         [(7168, 18432, 2), (7168, 7168, 4)] + [(2048, 7168, 32)] * 4
-    attn = nsa.plan_query([(2048, 2048)] * 32, torch.bfloat16)
+    attn = nsa.plan_query([(2048, 2048)] * 32, torch.bfloat16, compute_units=0)
     assert [b["count"] for b in attn["batches"]] == [32]
-    capped = nsa.plan_query([(2048, 2048)] * 32, torch.bfloat16, batch_cap_elems=5 * 2048 * 2048)
+    capped = nsa.plan_query([(2048, 2048)] * 32, torch.bfloat16, batch_cap_elems=5 * 2048 * 2048,
+                            compute_units=0)
     assert [b["count"] for b in capped["batches"]] == [5, 5, 5, 5, 4, 4, 4]
 
 
