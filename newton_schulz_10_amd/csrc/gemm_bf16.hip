@@ -5,14 +5,18 @@
 // matrices are concatenated along a batch axis and orthogonalized by one
 // batched NS iteration, a single sequence of batched matmuls, in bf16.
 // Per NS step and matrix (X is m x n, m <= n, zero padded):
-//   Gram   : A  = sc * X X^T              rows of X  . rows of X    (K = n)
-//   Poly   : B' = a*I + b*A + c*(A A^T)   rows of A  . rows of A    (K = m)
-//   Update : X' = sc * (B' X)             rows of B' . columns of X (K = m)
-// The page writes the step as X' = a X + B X with B = b A + c A A; here the
-// a X term is moved into the diagonal of B' (the same product, one more
-// rounding of the diagonal to bf16, relative 2^-9 of the a X term like the
-// rounding of X itself), so that Update needs no operand in its epilogue.
-// A and B' are symmetric: Gram and Poly compute only the tiles on or below
+//   Gram   : A' = sc * X X^T + beta I                 rows of X . rows of X    (K = n)
+//   Poly   : B' = c * (A' A'^T) + (a - b^2/(4c)) I    rows of A'. rows of A'   (K = m)
+//   Update : X' = sc * (B' X)                         rows of B'. columns of X (K = m)
+// with beta = b/(2c). The page writes the step as X' = a X + B X with
+// B = b A + c A A. Here the a X term moves into B' (the same product), and
+// the polynomial is completed to a square, a I + b A + c A^2 = c (A + beta
+// I)^2 + (a - b^2/(4c)) I, so neither Poly nor Update reads an operand tile
+// in its epilogue. Each changes one rounding: the diagonal of A' and of B'
+// is rounded to bf16 after the constant is added, an error of the order of
+// the rounding of A and X themselves. When c = 0 (a caller's coefficient
+// table) Gram writes A and Poly forms b A + c A A + a I with the A tile.
+// A' and B' are symmetric: Gram and Poly compute only the tiles on or below
 // the diagonal and store each one twice (tile and mirror). Update stores
 // X'. sc is the first step's Frobenius scale (s^2 for Gram, s for
 // Update) and 1 afterwards. Accumulation is fp32 on
@@ -382,7 +386,7 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& g, int mat, int I, int
     if (WIDE && (I == J || I == J + 1)) diag_off = (I - J) * TILE;
   }
 
-  if (ROLE == kPoly) {
+  if (ROLE == kPoly && g.poly_operand) {
     // Epilogue operand tile A into T: 128 loads of 1 KiB, 32 per wave; lane
     // l of a load takes stored chunk l % TC8 of its row, i.e. source chunk
     // (l % TC8) ^ eswz(row).
@@ -404,18 +408,21 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& g, int mat, int I, int
   // block at a time: all 16 operand reads of the block are issued before
   // any write (written in place, so the compiler would otherwise order
   // every read after the previous write).
-  //   Gram:   A  = sc * acc
-  //   Poly:   B' = a I + b A + c acc   (a on the diagonal: DG instance)
-  //   Update: X' = sc * acc            (acc = B' X)
+  //   Gram:   A' = sc * acc + d I          (d = diag_add: b/(2c), or 0)
+  //   Poly:   B' = c acc + d I             (acc = A'A', d = a - b^2/(4c))
+  //      or   B' = b A + c acc + a I       (operand tile A, when c = 0)
+  //   Update: X' = sc * acc                (acc = B' X)
+  // d is added by the DG instances, on diagonal tiles only.
   // A wave's block holds diagonal elements only if rb0 + diag_off == cb0;
   // then they sit in acc[b][b], element 4*(l/8) + l%4 (l = lane % 32) of
   // the lanes with lane/32 == (l/4) % 2.
   const int l32 = lane & 31;
   const int dsel = (diag_off >= 0 && rb0 + diag_off == cb0 && (lane >> 5) == ((l32 >> 2) & 1))
                        ? 4 * (l32 >> 3) + (l32 & 3) : -1;
-  auto form = [&](auto dg, auto scaled) {
+  auto form = [&](auto dg, auto scaled, auto opnd) {
     constexpr bool DG = decltype(dg)::value;
     constexpr bool SC = decltype(scaled)::value;
+    constexpr bool OP = decltype(opnd)::value;
 #pragma unroll
   for (int b = 0; b < 4; ++b) {
     const int i = rb0 + b * 32 + (lane & 31);
@@ -426,7 +433,7 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& g, int mat, int I, int
       return reinterpret_cast<uint2*>(row + (((j >> 3) ^ sw) << 3) + (j & 7));
     };
     uint2 w[4][4];
-    if (ROLE == kPoly) {
+    if (OP) {
 #pragma unroll
       for (int a = 0; a < 4; ++a)
 #pragma unroll
@@ -439,18 +446,21 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& g, int mat, int I, int
         float v[4];
 #pragma unroll
         for (int e = 0; e < 4; ++e) v[e] = acc[a][b][4 * q + e];
-        if (ROLE == kPoly) {
+        if (OP) {
           const float x[4] = {bf16_to_f32(w[a][q].x & 0xffffu), bf16_to_f32(w[a][q].x >> 16),
                               bf16_to_f32(w[a][q].y & 0xffffu), bf16_to_f32(w[a][q].y >> 16)};
 #pragma unroll
           for (int e = 0; e < 4; ++e) v[e] = fmaf(g.cb, x[e], g.cc * v[e]);
-          if (DG && a == b) {
+        } else if (ROLE == kPoly) {
 #pragma unroll
-            for (int e = 0; e < 4; ++e) v[e] += (4 * q + e == dsel) ? g.ca : 0.0f;
-          }
+          for (int e = 0; e < 4; ++e) v[e] *= g.cc;
         } else if (SC) {
 #pragma unroll
           for (int e = 0; e < 4; ++e) v[e] *= sc;
+        }
+        if (DG && a == b) {
+#pragma unroll
+          for (int e = 0; e < 4; ++e) v[e] += (4 * q + e == dsel) ? g.diag_add : 0.0f;
         }
         uint2 o;
         o.x = f32x2_to_bf16x2(v[0], v[1]);
@@ -460,12 +470,24 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& g, int mat, int I, int
     }
   }
   };
-  if (ROLE == kPoly && diag_off >= 0)
-    form(std::true_type{}, std::false_type{});
-  else if (ROLE != kPoly && g.scales)
-    form(std::false_type{}, std::true_type{});
-  else
-    form(std::false_type{}, std::false_type{});
+  using T1 = std::true_type;
+  using F0 = std::false_type;
+  const bool dgon = kSym && diag_off >= 0 && g.diag_add != 0.0f;
+  if (ROLE == kPoly) {
+    if (g.poly_operand) {
+      if (dgon) form(T1{}, F0{}, T1{}); else form(F0{}, F0{}, T1{});
+    } else {
+      if (dgon) form(T1{}, F0{}, F0{}); else form(F0{}, F0{}, F0{});
+    }
+  } else if (ROLE == kGram) {
+    if (g.scales) {
+      if (dgon) form(T1{}, T1{}, F0{}); else form(F0{}, T1{}, F0{});
+    } else {
+      if (dgon) form(T1{}, F0{}, F0{}); else form(F0{}, F0{}, F0{});
+    }
+  } else {
+    if (g.scales) form(F0{}, T1{}, F0{}); else form(F0{}, F0{}, F0{});
+  }
   __syncthreads();
 
   // A diagonal block needs no symmetrizing: element (i, j) and (j, i) are

@@ -88,6 +88,11 @@ struct GemmArgs {
   int m_pad, n_pad;
   const float* scales;  // per-matrix s (first iteration) or nullptr
   float ca, cb, cc;     // quintic coefficients of this step
+  // bf16 kernels only: the value added on the global diagonal by Gram (A'
+  // = A + diag_add I) and Poly, and whether Poly reads the A tile in its
+  // epilogue (b A + c A A + a I) or not (c A'A' + diag_add I).
+  float diag_add;
+  int poly_operand;
 };
 
 hipError_t launch_momentum(const EwMats& mats, const MomentumArgs& a, int src_bf16, int ws_bf16,

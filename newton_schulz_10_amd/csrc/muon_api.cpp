@@ -226,12 +226,23 @@ int run(const std::vector<MatRef>& mats, float lr, float beta, int ns_steps, muo
       g.ca = o.coeffs ? o.coeffs[3 * k + 0] : 3.4445f;
       g.cb = o.coeffs ? o.coeffs[3 * k + 1] : -4.7750f;
       g.cc = o.coeffs ? o.coeffs[3 * k + 2] : 2.0315f;
+      // bf16: with c != 0 the polynomial is completed to a square,
+      //   a I + b A + c A^2 = c (A + beta I)^2 + (a - b^2/(4c)) I,
+      //   beta = b / (2c),
+      // so Gram writes A' = A + beta I and Poly needs no A tile. The step's
+      // arithmetic is in double, rounded once to float.
+      const bool shifted = bf16 && g.cc != 0.0f;
+      const double beta_sq = shifted ? (double)g.cb / (2.0 * (double)g.cc) : 0.0;
+      const float gram_diag = (float)beta_sq;
+      const float poly_diag = shifted ? (float)((double)g.ca - (double)g.cb * (double)g.cb / (4.0 * (double)g.cc)) : g.ca;
       const GemmRole roles[3] = {kGram, kPoly, kUpdate};
       const char* names[3] = {"ns_gram", "ns_poly", "ns_update"};
       for (int r = 0; r < 3; ++r) {
         g.x = X; g.a = Am; g.b = Bm;
         g.out = r == 0 ? Am : (r == 1 ? Bm : Xn);
         g.scales = (k == 0 && r != 1) ? scales : nullptr;
+        g.diag_add = r == 0 ? gram_diag : (r == 1 ? poly_diag : 0.0f);
+        g.poly_operand = shifted ? 0 : 1;
         ProfScope ps(names[r], gemm_flops(roles[r], g), 0.0, stream);
         e = bf16 ? launch_gemm_bf16(roles[r], g, stream) : launch_gemm_f32(roles[r], g, stream);
         if (e != hipSuccess) { status = hip_fail(e, names[r]); break; }

@@ -117,6 +117,19 @@ def test_coefficient_table(nsa):
         assert_parity(case, dtype, p1, m1, ref, tol)
 
 
+def test_coefficient_table_with_cubic_steps(nsa):
+    # c = 0 in two steps: the cubic Newton-Schulz step X <- 1.5 X - 0.5 X X^T X.
+    # The bf16 path completes a I + b A + c A^2 to a square only when c != 0;
+    # these steps take the other form (b A + a I with the A tile).
+    table = [(3.4445, -4.775, 2.0315), (1.5, -0.5, 0.0), (3.4445, -4.775, 2.0315), (1.5, -0.5, 0.0),
+             (3.4445, -4.775, 2.0315)]
+    for dtype, tol in (("f32", F32_TOL), ("bf16", BF16_TOL)):
+        case = workloads.random_case(14, [(192, 320), (320, 192), (300, 520)], dtype, params_init="zero")
+        p1, m1 = run_case(nsa, case, dtype, coeffs=table)
+        ref = oracle_case(case, 0.02, 0.95, 5, coeffs=table)
+        assert_parity(case, dtype, p1, m1, ref, tol)
+
+
 @pytest.mark.parametrize("steps", [0, 1, 2])
 def test_few_ns_steps(nsa, steps):
     for dtype, tol in (("f32", F32_TOL), ("bf16", BF16_TOL)):
