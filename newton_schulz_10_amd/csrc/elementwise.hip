@@ -42,6 +42,30 @@ __device__ __forceinline__ void load4(const ST* p, int valid, float v[4]) {
   }
 }
 
+// 4 whole elements at a 4-element-aligned address (interior tiles).
+template <typename ST>
+__device__ __forceinline__ void load4a(const ST* p, float v[4]) {
+  if constexpr (sizeof(ST) == 4) {
+    const float4 q = *reinterpret_cast<const float4*>(p);
+    v[0] = q.x; v[1] = q.y; v[2] = q.z; v[3] = q.w;
+  } else {
+    const uint2 q = *reinterpret_cast<const uint2*>(p);
+    v[0] = bf16_to_f32(q.x & 0xffffu); v[1] = bf16_to_f32(q.x >> 16);
+    v[2] = bf16_to_f32(q.y & 0xffffu); v[3] = bf16_to_f32(q.y >> 16);
+  }
+}
+template <typename ST>
+__device__ __forceinline__ void store4a(ST* p, const float v[4]) {
+  if constexpr (sizeof(ST) == 4) {
+    *reinterpret_cast<float4*>(p) = make_float4(v[0], v[1], v[2], v[3]);
+  } else {
+    uint2 q;
+    q.x = f32x2_to_bf16x2(v[0], v[1]);
+    q.y = f32x2_to_bf16x2(v[2], v[3]);
+    *reinterpret_cast<uint2*>(p) = q;
+  }
+}
+
 template <typename ST>
 __device__ __forceinline__ void store4(ST* p, int valid, const float v[4]) {
   if (valid == 4 && (reinterpret_cast<uintptr_t>(p) % (4 * sizeof(ST)) == 0)) {
@@ -83,7 +107,62 @@ __global__ __launch_bounds__(256) void momentum_kernel(EwMats mats, MomentumArgs
   XT* x0 = static_cast<XT*>(a.x0) + (size_t)(a.first + mi) * a.mat_x;
   float ss = 0.0f;
 
-  if (!mats.tr[mi]) {
+  // Interior tiles (all 64 x 64 elements in range, rows a multiple of 4
+  // long, so every 4-element access is whole and aligned) issue all their
+  // loads before any arithmetic or store: four passes of loads in flight
+  // per thread instead of one. Edge tiles take the general path below.
+  const int orig_cols = mats.tr[mi] ? a.m : a.n;   // row length of the original
+  const bool interior = (orig_cols % 4 == 0) && (ti + 1) * T <= a.m && (tj + 1) * T <= a.n;
+  if (interior && !mats.tr[mi]) {
+    float gv[4][4], bv[4][4];
+#pragma unroll
+    for (int p = 0; p < 4; ++p) {
+      const size_t off = (size_t)(ti * T + ty + 16 * p) * a.n + tj * T + tx * 4;
+      load4a<GT>(g + off, gv[p]);
+      if (a.has_buf) load4a<float>(buf + off, bv[p]);
+    }
+#pragma unroll
+    for (int p = 0; p < 4; ++p) {
+      const int i = ti * T + ty + 16 * p;
+      const size_t off = (size_t)i * a.n + tj * T + tx * 4;
+      float u[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        u[e] = momentum_elem(gv[p][e], bv[p][e], a);
+        ss = fmaf(u[e], u[e], ss);
+      }
+      if (a.has_buf) store4a<float>(buf + off, bv[p]);
+      store4a<XT>(x0 + (size_t)i * a.n_pad + tj * T + tx * 4, u);
+    }
+  } else if (interior) {
+    float gv[4][4], bv[4][4];
+#pragma unroll
+    for (int p = 0; p < 4; ++p) {
+      const size_t off = (size_t)(tj * T + ty + 16 * p) * a.m + ti * T + tx * 4;
+      load4a<GT>(g + off, gv[p]);
+      if (a.has_buf) load4a<float>(buf + off, bv[p]);
+    }
+#pragma unroll
+    for (int p = 0; p < 4; ++p) {
+      const size_t off = (size_t)(tj * T + ty + 16 * p) * a.m + ti * T + tx * 4;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const float u = momentum_elem(gv[p][e], bv[p][e], a);
+        ss = fmaf(u, u, ss);
+        tile[ty + 16 * p][tx * 4 + e] = u;
+      }
+      if (a.has_buf) store4a<float>(buf + off, bv[p]);
+    }
+    __syncthreads();
+#pragma unroll
+    for (int p = 0; p < 4; ++p) {
+      const int il = ty + 16 * p, jl = tx * 4;
+      float v[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) v[e] = tile[jl + e][il];
+      store4a<XT>(x0 + (size_t)(ti * T + il) * a.n_pad + tj * T + jl, v);
+    }
+  } else if (!mats.tr[mi]) {
     // Stored wide: element (i, j) of the m x n matrix is X0[i][j].
 #pragma unroll
     for (int p = 0; p < 4; ++p) {
@@ -169,6 +248,53 @@ __global__ __launch_bounds__(256) void apply_kernel(EwMats mats, ApplyArgs a) {
   const float gamma = a.gamma[tr];
   PT* dst = static_cast<PT*>(mats.dst[mi]);
   const PT* src = static_cast<const PT*>(mats.src[mi]);
+
+  // Interior tiles: all loads first (see momentum_kernel).
+  const bool interior = ((tr ? a.m : a.n) % 4 == 0) && (ti + 1) * T <= a.m && (tj + 1) * T <= a.n;
+  if (interior && !tr) {
+    float o[4][4], pv[4][4];
+#pragma unroll
+    for (int p = 0; p < 4; ++p) {
+      const int i = ti * T + ty + 16 * p, j = tj * T + tx * 4;
+      load4a<XT>(x + (size_t)i * a.n_pad + j, o[p]);
+      if (a.mode == 0) load4a<PT>(src + (size_t)i * a.n + j, pv[p]);
+    }
+#pragma unroll
+    for (int p = 0; p < 4; ++p) {
+      const int i = ti * T + ty + 16 * p, j = tj * T + tx * 4;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const float oe = o[p][e] * os;
+        pv[p][e] = a.mode == 0 ? fmaf(-gamma, oe, a.alpha * pv[p][e]) : oe;
+      }
+      store4a<PT>(dst + (size_t)i * a.n + j, pv[p]);
+    }
+    return;
+  }
+  if (interior) {
+    float o[4][4], pv[4][4];
+#pragma unroll
+    for (int p = 0; p < 4; ++p) {
+      load4a<XT>(x + (size_t)(ti * T + ty + 16 * p) * a.n_pad + tj * T + tx * 4, o[p]);
+      if (a.mode == 0) load4a<PT>(src + (size_t)(tj * T + ty + 16 * p) * a.m + ti * T + tx * 4, pv[p]);
+    }
+#pragma unroll
+    for (int p = 0; p < 4; ++p)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) tile[ty + 16 * p][tx * 4 + e] = o[p][e];
+    __syncthreads();
+#pragma unroll
+    for (int p = 0; p < 4; ++p) {
+      const int r = tj * T + ty + 16 * p, c = ti * T + tx * 4;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const float oe = tile[tx * 4 + e][ty + 16 * p] * os;
+        pv[p][e] = a.mode == 0 ? fmaf(-gamma, oe, a.alpha * pv[p][e]) : oe;
+      }
+      store4a<PT>(dst + (size_t)r * a.m + c, pv[p]);
+    }
+    return;
+  }
 
   if (!tr) {
 #pragma unroll
