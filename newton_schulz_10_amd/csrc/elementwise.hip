@@ -106,6 +106,7 @@ __global__ __launch_bounds__(256) void momentum_kernel(EwMats mats, MomentumArgs
   float* buf = mats.buf[mi];
   XT* x0 = static_cast<XT*>(a.x0) + (size_t)(a.first + mi) * a.mat_x;
   float ss = 0.0f;
+  if (a.ptab && blockIdx.x == 0 && threadIdx.x == 0) a.ptab[a.first + mi] = ApplyEntry{mats.dst[mi], mats.tr[mi], 0};
 
   // Interior tiles (all 64 x 64 elements in range, rows a multiple of 4
   // long, so every 4-element access is whole and aligned) issue all their

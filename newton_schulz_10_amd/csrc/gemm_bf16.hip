@@ -511,9 +511,85 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& g, int mat, int I, int
     }
     return __builtin_bit_cast(uint4, __builtin_shufflevector(h[0], h[1], 0, 1, 2, 3, 4, 5, 6, 7));
   };
+  constexpr int kBatch = 8;
+  if constexpr (ROLE == kUpdate) {
+    if (g.ptab) {
+      // Last step with the apply fused: X' (rounded to bf16 in T, the same
+      // O the separate pass reads) goes straight into the parameter,
+      // p' = alpha*p - gamma*O (or out = O), with that pass's arithmetic,
+      // in the matrix's original orientation; X' itself is not stored.
+      // Reads of a batch (T, then p) are issued before its stores.
+      const ApplyEntry ent = g.ptab[mat];
+      bf16_t* const dst = static_cast<bf16_t*>(ent.dst);
+      const float gam = g.gamma[ent.tr], alpha = g.alpha;
+      const bool upd = g.apply_mode == 0;
+      auto apply8 = [&](uint4 o, uint4 pv) {
+        if (!upd) return o;
+        const unsigned ow[4] = {o.x, o.y, o.z, o.w}, pw[4] = {pv.x, pv.y, pv.z, pv.w};
+        unsigned r[4];
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+          const float r0 = fmaf(-gam, bf16_to_f32(ow[k] & 0xffffu), alpha * bf16_to_f32(pw[k] & 0xffffu));
+          const float r1 = fmaf(-gam, bf16_to_f32(ow[k] >> 16), alpha * bf16_to_f32(pw[k] >> 16));
+          r[k] = f32x2_to_bf16x2(r0, r1);
+        }
+        return uint4{r[0], r[1], r[2], r[3]};
+      };
+      if (!ent.tr) {
+        // Wide member: tile rows are rows of p (row length n).
+#pragma unroll 1
+        for (int r0 = 0; r0 < (PR * TC8) / kThreads; r0 += kBatch) {
+          uint4 v[kBatch], pv[kBatch];
+          size_t off[kBatch];
+          bool ok[kBatch];
+#pragma unroll
+          for (int u = 0; u < kBatch; ++u) {
+            const int id = (r0 + u) * kThreads + tid;
+            const int i = id / TC8, c = id % TC8;
+            v[u] = *reinterpret_cast<const uint4*>(T + i * QR + ((c ^ eswz(i)) << 3));
+            const int gi = I * TILE + i, gj = q0 + 8 * c;
+            ok[u] = gi < g.m && gj < g.n;
+            off[u] = ok[u] ? (size_t)gi * g.n + gj : 0;
+            pv[u] = upd ? *reinterpret_cast<const uint4*>(dst + off[u]) : uint4{0u, 0u, 0u, 0u};
+          }
+          keep_batch(v);
+          keep_batch(pv);
+#pragma unroll
+          for (int u = 0; u < kBatch; ++u)
+            if (ok[u]) *reinterpret_cast<uint4*>(dst + off[u]) = apply8(v[u], pv[u]);
+        }
+      } else {
+        // Tall member: p is n x m; wide element (i, j) is p[j][i]. A
+        // transposing gather gives 8 consecutive wide rows of one column.
+        constexpr int NJ = QR / 16, NI = PR / 32;
+#pragma unroll 1
+        for (int r0 = wave; r0 < NJ * NI; r0 += 4 * kBatch) {
+          uint4 v[kBatch], pv[kBatch];
+          size_t off[kBatch];
+          bool ok[kBatch];
+#pragma unroll
+          for (int u = 0; u < kBatch; ++u) {
+            const int r = r0 + 4 * u;
+            const int jb = (r / NI) * 16, i0 = (r % NI) * 32;
+            v[u] = tr8(i0, jb);
+            const int gj = q0 + jb + jj, gi = I * TILE + i0 + 8 * grp;
+            ok[u] = gj < g.n && gi < g.m;
+            off[u] = ok[u] ? (size_t)gj * g.m + gi : 0;
+            pv[u] = upd ? *reinterpret_cast<const uint4*>(dst + off[u]) : uint4{0u, 0u, 0u, 0u};
+          }
+          keep_batch(v);
+          keep_batch(pv);
+#pragma unroll
+          for (int u = 0; u < kBatch; ++u)
+            if (ok[u]) *reinterpret_cast<uint4*>(dst + off[u]) = apply8(v[u], pv[u]);
+        }
+      }
+      return;
+    }
+  }
+
   // Tile rows -> out: TC8 lanes store one row. Reads go in batches of 8
   // ahead of their stores, so the LDS latency is paid once per batch.
-  constexpr int kBatch = 8;
   // Uniform tile base plus 32-bit per-lane offsets (scalar-base addressing).
   bf16_t* const otile = out + (size_t)(I * TILE) * ldo + q0;
 #pragma unroll
@@ -640,7 +716,11 @@ hipError_t device_cu_count(int* out) {
 }  // namespace
 
 hipError_t launch_gemm_bf16(GemmRole role, const GemmArgs& g, hipStream_t s) {
+  static_assert(sizeof(ApplyEntry) == 16, "the workspace reserves 16 B per fused-apply entry");
   if (g.count <= 0) return hipSuccess;
+  // The fused apply stores 8 elements (16 B) per access along rows of both
+  // orientations.
+  if (role == kUpdate && g.ptab && (g.m % 8 || g.n % 8)) return hipErrorInvalidValue;
   // m is padded to 128, n to 256 (so X'^T rows and the K of Gram are whole
   // tiles); m <= n.
   if (g.m_pad <= 0 || g.m_pad % 128 || g.n_pad % TILE || g.m_pad > g.n_pad) return hipErrorInvalidValue;

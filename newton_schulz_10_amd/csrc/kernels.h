@@ -21,6 +21,15 @@ struct EwMats {
   unsigned char tr[kEwChunk]; // 1 when the matrix is stored tall (rows > cols)
 };
 
+// Where the parameter update of one matrix goes, for the apply fused into
+// the last Update GEMM: written per matrix by the momentum pass (whose
+// kernel arguments carry the pointers), read per tile by the GEMM.
+struct ApplyEntry {
+  void* dst;   // param, updated in place (step), or the output (orthogonalize)
+  int tr;      // 1 when the matrix is stored tall (rows > cols)
+  int pad;
+};
+
 // Momentum pass: reads each matrix's source (and momentum buffer), writes
 // the buffer, the wide zero-padded NS input X0 = u (rounded to the
 // workspace type), optionally its transpose X0^T, and one fp32 partial sum
@@ -38,6 +47,7 @@ struct MomentumArgs {
   float beta;               // buf' = beta*buf + kg*g
   float kg;                 // 1-beta (EMA) or 1 (heavy ball)
   int nesterov;             // u = kg*g + beta*buf' if 1, else buf'
+  ApplyEntry* ptab;         // [batch matrices] entries to fill (dst, tr), or nullptr
 };
 
 // Norm finalize: scales[i] = 1 / (sqrt(sum_k partials[i][k]) + eps).
@@ -93,6 +103,13 @@ struct GemmArgs {
   // epilogue (b A + c A A + a I) or not (c A'A' + diag_add I).
   float diag_add;
   int poly_operand;
+  // bf16 Update only: when ptab is set, the tile is not stored as X' but
+  // applied: p' = alpha*p - gamma[tr]*O (apply_mode 0) or out = O (1), O
+  // being X' rounded to bf16, in the matrix's original orientation.
+  const ApplyEntry* ptab;
+  float alpha;
+  float gamma[2];
+  int apply_mode;
 };
 
 hipError_t launch_momentum(const EwMats& mats, const MomentumArgs& a, int src_bf16, int ws_bf16,

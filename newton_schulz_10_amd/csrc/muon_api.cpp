@@ -183,7 +183,14 @@ int run(const std::vector<MatRef>& mats, float lr, float beta, int ns_steps, muo
     void* Bm = W + L.b;
     float* partials = reinterpret_cast<float*>(W + L.partials);
     float* scales = reinterpret_cast<float*>(W + L.scales);
+    ApplyEntry* ptab = reinterpret_cast<ApplyEntry*>(W + L.ptab);
     const double elems = (double)B.m * B.n;
+    // bf16 with at least one NS step: the apply runs inside the last Update
+    // GEMM (it needs whole 16 B runs along rows of both orientations).
+    const bool fused_apply = bf16 && ns_steps > 0 && B.m % 8 == 0 && B.n % 8 == 0;
+    const float apply_alpha = (float)(1.0 - (double)lr * (double)o.weight_decay);
+    const float apply_gamma[2] = {(float)((double)lr * update_scale(o, B.m, B.n)),
+                                  (float)((double)lr * update_scale(o, B.n, B.m))};
 
     // 1. momentum (+ transpose, cast, partial sums)
     for (int c0 = 0; c0 < B.count && status == MUON_OK; c0 += kEwChunk) {
@@ -194,6 +201,7 @@ int run(const std::vector<MatRef>& mats, float lr, float beta, int ns_steps, muo
         const MatRef& r = mats[plan.order[B.first + c0 + k]];
         em.src[k] = r.src;
         em.buf[k] = r.mom;
+        em.dst[k] = r.param;
         em.tr[k] = r.rows > r.cols ? 1 : 0;
       }
       MomentumArgs a;
@@ -201,6 +209,7 @@ int run(const std::vector<MatRef>& mats, float lr, float beta, int ns_steps, muo
       a.ew_blocks = L.ew_blocks; a.first = c0; a.x0 = x0; a.mat_x = L.mat_x;
       a.partials = partials; a.has_buf = orthogonalize_only ? 0 : 1;
       a.beta = beta; a.kg = kg; a.nesterov = o.nesterov;
+      a.ptab = fused_apply ? ptab : nullptr;
       const double bytes = cn * elems * ((orthogonalize_only ? es : es + 4 + 4) + es);
       ProfScope ps("momentum", 0.0, bytes, stream);
       e = launch_momentum(em, a, bf16, bf16, stream);
@@ -220,7 +229,7 @@ int run(const std::vector<MatRef>& mats, float lr, float beta, int ns_steps, muo
     void* X = x0;
     void* Xn = x1;
     for (int k = 0; k < ns_steps && status == MUON_OK; ++k) {
-      GemmArgs g;
+      GemmArgs g{};
       g.mat_x = L.mat_x; g.mat_a = L.mat_a; g.count = B.count;
       g.m = B.m; g.n = B.n; g.m_pad = B.m_pad; g.n_pad = B.n_pad;
       g.ca = o.coeffs ? o.coeffs[3 * k + 0] : 3.4445f;
@@ -243,6 +252,12 @@ int run(const std::vector<MatRef>& mats, float lr, float beta, int ns_steps, muo
         g.scales = (k == 0 && r != 1) ? scales : nullptr;
         g.diag_add = r == 0 ? gram_diag : (r == 1 ? poly_diag : 0.0f);
         g.poly_operand = shifted ? 0 : 1;
+        const bool apply_here = fused_apply && r == 2 && k + 1 == ns_steps;
+        g.ptab = apply_here ? ptab : nullptr;
+        g.alpha = apply_alpha;
+        g.gamma[0] = apply_gamma[0];
+        g.gamma[1] = apply_gamma[1];
+        g.apply_mode = orthogonalize_only ? 1 : 0;
         ProfScope ps(names[r], gemm_flops(roles[r], g), 0.0, stream);
         e = bf16 ? launch_gemm_bf16(roles[r], g, stream) : launch_gemm_f32(roles[r], g, stream);
         if (e != hipSuccess) { status = hip_fail(e, names[r]); break; }
@@ -251,8 +266,8 @@ int run(const std::vector<MatRef>& mats, float lr, float beta, int ns_steps, muo
     }
     if (status) break;
 
-    // 4. apply (+ transpose back)
-    for (int c0 = 0; c0 < B.count && status == MUON_OK; c0 += kEwChunk) {
+    // 4. apply (+ transpose back), unless the last Update did it
+    for (int c0 = 0; c0 < B.count && status == MUON_OK && !fused_apply; c0 += kEwChunk) {
       const int cn = std::min(kEwChunk, B.count - c0);
       EwMats em;
       std::memset(&em, 0, sizeof(em));
@@ -266,9 +281,9 @@ int run(const std::vector<MatRef>& mats, float lr, float beta, int ns_steps, muo
       a.count = cn; a.m = B.m; a.n = B.n; a.n_pad = B.n_pad; a.first = c0;
       a.x = X; a.mat_x = L.mat_x; a.scales = scales; a.use_scale = ns_steps == 0 ? 1 : 0;
       a.mode = orthogonalize_only ? 1 : 0;
-      a.alpha = (float)(1.0 - (double)lr * (double)o.weight_decay);
-      a.gamma[0] = (float)((double)lr * update_scale(o, B.m, B.n));
-      a.gamma[1] = (float)((double)lr * update_scale(o, B.n, B.m));
+      a.alpha = apply_alpha;
+      a.gamma[0] = apply_gamma[0];
+      a.gamma[1] = apply_gamma[1];
       const double bytes = cn * elems * (orthogonalize_only ? es + es : es + es + es);
       ProfScope ps("apply", 0.0, bytes, stream);
       e = launch_apply(em, a, bf16, bf16, stream);

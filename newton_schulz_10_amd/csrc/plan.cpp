@@ -34,6 +34,7 @@ Layout batch_layout(int count, int m_pad, int n_pad, muon_dtype dtype) {
   L.b = off;        off = align_up(off + (size_t)count * L.mat_a * es, A);
   L.partials = off; off = align_up(off + (size_t)count * (size_t)L.ew_blocks * sizeof(float), A);
   L.scales = off;   off = align_up(off + (size_t)count * sizeof(float), A);
+  L.ptab = off;     off = align_up(off + (size_t)count * 16, A);   // fused-apply entries
   L.total = off;
   return L;
 }

@@ -108,6 +108,19 @@ def test_bf16_nonzero_params_weight_decay(nsa):
     assert_parity(case, "bf16", p1, m1, ref, BF16_TOL)
 
 
+def test_bf16_fused_apply_orientation_scale(nsa):
+    # bf16 shapes with rows and columns multiples of 8 take the apply fused
+    # into the last Update GEMM. scale_rule "original" (sqrt(max(1, rows/cols)))
+    # differs between a matrix and its transpose, so wide and tall members
+    # must each get their own factor; nonzero params and weight decay
+    # exercise p' = alpha*p - gamma*O. The 300x520 member (rows not a
+    # multiple of 8) takes the separate apply pass in the same call.
+    case = workloads.random_case(15, [(256, 384), (384, 256), (128, 640), (640, 128), (300, 520)], "bf16")
+    p1, m1 = run_case(nsa, case, "bf16", 0.02, 0.95, 5, weight_decay=0.05, scale_rule="original")
+    ref = oracle_case(case, 0.02, 0.95, 5, weight_decay=0.05, scale_rule="original")
+    assert_parity(case, "bf16", p1, m1, ref, BF16_TOL)
+
+
 def test_coefficient_table(nsa):
     table = [(3.0, -3.2, 1.2), (3.4445, -4.775, 2.0315), (2.9, -3.0, 1.1), (3.4, -4.7, 2.0), (1.875, -1.25, 0.375)]
     for dtype, tol in (("f32", F32_TOL), ("bf16", BF16_TOL)):
