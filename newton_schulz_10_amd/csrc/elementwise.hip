@@ -106,6 +106,7 @@ __global__ __launch_bounds__(256) void momentum_kernel(EwMats mats, MomentumArgs
   float* buf = mats.buf[mi];
   XT* x0 = static_cast<XT*>(a.x0) + (size_t)(a.first + mi) * a.mat_x;
   float ss = 0.0f;
+  int nz = 0;   // any u of the tile not exactly 0 (NaN != 0 counts)
   if (a.ptab && blockIdx.x == 0 && threadIdx.x == 0) a.ptab[a.first + mi] = ApplyEntry{mats.dst[mi], mats.tr[mi], 0};
 
   // Interior tiles (all 64 x 64 elements in range, rows a multiple of 4
@@ -131,6 +132,7 @@ __global__ __launch_bounds__(256) void momentum_kernel(EwMats mats, MomentumArgs
       for (int e = 0; e < 4; ++e) {
         u[e] = momentum_elem(gv[p][e], bv[p][e], a);
         ss = fmaf(u[e], u[e], ss);
+        nz |= u[e] != 0.0f;
       }
       if (a.has_buf) store4a<float>(buf + off, bv[p]);
       store4a<XT>(x0 + (size_t)i * a.n_pad + tj * T + tx * 4, u);
@@ -150,6 +152,7 @@ __global__ __launch_bounds__(256) void momentum_kernel(EwMats mats, MomentumArgs
       for (int e = 0; e < 4; ++e) {
         const float u = momentum_elem(gv[p][e], bv[p][e], a);
         ss = fmaf(u, u, ss);
+        nz |= u != 0.0f;
         tile[ty + 16 * p][tx * 4 + e] = u;
       }
       if (a.has_buf) store4a<float>(buf + off, bv[p]);
@@ -180,6 +183,7 @@ __global__ __launch_bounds__(256) void momentum_kernel(EwMats mats, MomentumArgs
           if (e < valid) {
             u[e] = momentum_elem(gv[e], bv[e], a);
             ss = fmaf(u[e], u[e], ss);
+            nz |= u[e] != 0.0f;
           }
         }
         if (a.has_buf) store4<float>(buf + (size_t)i * a.n + j, valid, bv);
@@ -205,6 +209,7 @@ __global__ __launch_bounds__(256) void momentum_kernel(EwMats mats, MomentumArgs
           if (e < valid) {
             u[e] = momentum_elem(gv[e], bv[e], a);
             ss = fmaf(u[e], u[e], ss);
+            nz |= u[e] != 0.0f;
           }
         }
         if (a.has_buf) store4<float>(buf + (size_t)r * a.m + c, valid, bv);
@@ -223,7 +228,11 @@ __global__ __launch_bounds__(256) void momentum_kernel(EwMats mats, MomentumArgs
     }
   }
   const float tot = block_sum_256(ss, red);
-  if (threadIdx.x == 0) a.partials[(size_t)(a.first + mi) * a.ew_blocks + blockIdx.x] = tot;
+  const int any = __syncthreads_or(nz);
+  if (threadIdx.x == 0) {
+    a.partials[(size_t)(a.first + mi) * a.ew_blocks + blockIdx.x] = tot;
+    a.nonzero[(size_t)(a.first + mi) * a.ew_blocks + blockIdx.x] = any ? 1 : 0;
+  }
 }
 
 __global__ __launch_bounds__(256) void finalize_kernel(FinalizeArgs a) {
@@ -231,9 +240,17 @@ __global__ __launch_bounds__(256) void finalize_kernel(FinalizeArgs a) {
   const int mi = blockIdx.x;
   const float* p = a.partials + (size_t)mi * a.ew_blocks;
   float s = 0.0f;
-  for (int k = threadIdx.x; k < a.ew_blocks; k += 256) s += p[k];
+  int nz = 0;
+  for (int k = threadIdx.x; k < a.ew_blocks; k += 256) {
+    s += p[k];
+    nz |= a.nonzero[(size_t)mi * a.ew_blocks + k];
+  }
   const float tot = block_sum_256(s, red);
-  if (threadIdx.x == 0) a.scales[mi] = 1.0f / (sqrtf(tot) + a.eps);
+  const int any = __syncthreads_or(nz);
+  if (threadIdx.x == 0) {
+    a.scales[mi] = 1.0f / (sqrtf(tot) + a.eps);
+    a.live[mi] = any ? 1 : 0;
+  }
 }
 
 template <typename PT, typename XT>
@@ -247,6 +264,10 @@ __global__ __launch_bounds__(256) void apply_kernel(EwMats mats, ApplyArgs a) {
   const float os = a.use_scale ? a.scales[a.first + mi] : 1.0f;
   const int tr = mats.tr[mi];
   const float gamma = a.gamma[tr];
+  // A matrix whose NS input was exactly zero has O = 0 exactly (its iterate
+  // was not stored); with dead_only, live matrices are someone else's.
+  const bool zo = a.live != nullptr && a.live[a.first + mi] == 0;
+  if (a.dead_only && !zo) return;
   PT* dst = static_cast<PT*>(mats.dst[mi]);
   const PT* src = static_cast<const PT*>(mats.src[mi]);
 
@@ -258,6 +279,7 @@ __global__ __launch_bounds__(256) void apply_kernel(EwMats mats, ApplyArgs a) {
     for (int p = 0; p < 4; ++p) {
       const int i = ti * T + ty + 16 * p, j = tj * T + tx * 4;
       load4a<XT>(x + (size_t)i * a.n_pad + j, o[p]);
+      if (zo) o[p][0] = o[p][1] = o[p][2] = o[p][3] = 0.0f;
       if (a.mode == 0) load4a<PT>(src + (size_t)i * a.n + j, pv[p]);
     }
 #pragma unroll
@@ -277,6 +299,7 @@ __global__ __launch_bounds__(256) void apply_kernel(EwMats mats, ApplyArgs a) {
 #pragma unroll
     for (int p = 0; p < 4; ++p) {
       load4a<XT>(x + (size_t)(ti * T + ty + 16 * p) * a.n_pad + tj * T + tx * 4, o[p]);
+      if (zo) o[p][0] = o[p][1] = o[p][2] = o[p][3] = 0.0f;
       if (a.mode == 0) load4a<PT>(src + (size_t)(tj * T + ty + 16 * p) * a.m + ti * T + tx * 4, pv[p]);
     }
 #pragma unroll
@@ -307,6 +330,7 @@ __global__ __launch_bounds__(256) void apply_kernel(EwMats mats, ApplyArgs a) {
       if (valid == 0) continue;
       float o[4], pv[4] = {0.f, 0.f, 0.f, 0.f};
       load4<XT>(x + (size_t)i * a.n_pad + j, 4, o);
+      if (zo) o[0] = o[1] = o[2] = o[3] = 0.0f;
       if (a.mode == 0) load4<PT>(src + (size_t)i * a.n + j, valid, pv);
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
@@ -322,6 +346,7 @@ __global__ __launch_bounds__(256) void apply_kernel(EwMats mats, ApplyArgs a) {
       const int il = ty + 16 * p;
       float o[4];
       load4<XT>(x + (size_t)(ti * T + il) * a.n_pad + tj * T + tx * 4, 4, o);
+      if (zo) o[0] = o[1] = o[2] = o[3] = 0.0f;
 #pragma unroll
       for (int e = 0; e < 4; ++e) tile[il][tx * 4 + e] = o[e];
     }
@@ -345,7 +370,36 @@ __global__ __launch_bounds__(256) void apply_kernel(EwMats mats, ApplyArgs a) {
   }
 }
 
+// One workgroup: the live flags of a batch -> the ascending list of live
+// matrices and its length (a block-wide scan of per-thread counts).
+__global__ __launch_bounds__(256) void compact_kernel(const int* live, int count, int* list, int* nlive) {
+  __shared__ int sums[256];
+  const int t = threadIdx.x;
+  const int per = (count + 255) / 256;
+  const int lo = t * per, hi = min(count, lo + per);
+  int c = 0;
+  for (int i = lo; i < hi; ++i) c += live[i] != 0;
+  sums[t] = c;
+  __syncthreads();
+  for (int off = 1; off < 256; off <<= 1) {
+    const int v = t >= off ? sums[t - off] : 0;
+    __syncthreads();
+    sums[t] += v;
+    __syncthreads();
+  }
+  int pos = sums[t] - c;
+  for (int i = lo; i < hi; ++i)
+    if (live[i] != 0) list[pos++] = i;
+  if (t == 255) *nlive = sums[255];
+}
+
 }  // namespace
+
+hipError_t launch_compact(const int* live, int count, int* live_list, int* nlive, hipStream_t s) {
+  if (count <= 0) return hipSuccess;
+  hipLaunchKernelGGL(compact_kernel, dim3(1), dim3(256), 0, s, live, count, live_list, nlive);
+  return hipGetLastError();
+}
 
 hipError_t launch_momentum(const EwMats& mats, const MomentumArgs& a, int src_bf16, int ws_bf16,
                            hipStream_t s) {

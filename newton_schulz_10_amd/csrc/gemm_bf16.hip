@@ -642,14 +642,10 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& g, int mat, int I, int
   }
 }
 
-// One grid covers every tile of every matrix of the batch.
-//  * gridDim.x >= tiles: one tile per workgroup, block ids remapped so that
-//    each XCD (blocks are dealt round-robin over the 8 XCDs) works on a
-//    contiguous range of tiles, i.e. on whole matrices (L2 reuse).
-//  * otherwise (gridDim.x = one workgroup per CU, a multiple of 8): each
-//    workgroup loops over the tiles of its XCD's contiguous range, slot s
-//    taking tiles s, s + slots, ... (one launch of resident workgroups
-//    instead of one per tile).
+// One grid covers every tile of every computed matrix of the batch: at
+// most one workgroup per CU, a multiple of 8, each looping over the tiles
+// of its XCD's contiguous range (slot s taking tiles s, s + slots, ...), so
+// each XCD's L2 serves whole matrices.
 // Tile order within a matrix: full tiles (row-major over the lower triangle
 // for A/B, over all rows x columns for X'), then the wide tiles of the
 // half row.
@@ -659,23 +655,23 @@ void ns_gemm_bf16(GemmArgs g) {
   __shared__ __attribute__((aligned(1024))) Stages lds;
   constexpr bool kSym = (ROLE != kUpdate);
   const Geom G = geom(g, kSym);
-  const int total = G.per_mat * g.count;
-  int t, t_end, step;
-  if ((int)gridDim.x >= total) {
-    t = xcd_remap(blockIdx.x, total);
-    t_end = t + 1;
-    step = 1;
-  } else {
-    constexpr int kXcd = 8;
-    const int xcd = blockIdx.x % kXcd, slot = blockIdx.x / kXcd;
-    const int base = total / kXcd, rem = total % kXcd;
-    t = xcd * base + (xcd < rem ? xcd : rem) + slot;
-    t_end = xcd * base + (xcd < rem ? xcd : rem) + base + (xcd < rem ? 1 : 0);
-    step = gridDim.x / kXcd;
-  }
+  // Matrices to compute: all of the batch, or the live ones listed on the
+  // device (exactly-zero inputs, idle experts, are left out: their iterate
+  // stays zero and their update needs no product).
+  const int nmat = g.live_list ? *g.nlive : g.count;
+  const int total = G.per_mat * nmat;
+  // The grid is a multiple of 8: each XCD (blocks are dealt round-robin
+  // over the 8 XCDs) takes a contiguous range of tiles, i.e. whole
+  // matrices, and its slot s takes tiles s, s + slots, ... of that range.
+  constexpr int kXcd = 8;
+  const int xcd = blockIdx.x % kXcd, slot = blockIdx.x / kXcd;
+  const int base = total / kXcd, rem = total % kXcd;
+  int t = xcd * base + (xcd < rem ? xcd : rem) + slot;
+  const int t_end = xcd * base + (xcd < rem ? xcd : rem) + base + (xcd < rem ? 1 : 0);
+  const int step = gridDim.x / kXcd;
 #pragma nounroll
   for (; t < t_end; t += step) {
-    const int mat = t / G.per_mat;
+    const int mat = g.live_list ? g.live_list[t / G.per_mat] : t / G.per_mat;
     const int u = t % G.per_mat;
     if (u < G.full) {
       int I, J;
@@ -733,8 +729,10 @@ hipError_t launch_gemm_bf16(GemmRole role, const GemmArgs& g, hipStream_t s) {
   int cus = 0;
   hipError_t e = device_cu_count(&cus);
   if (e != hipSuccess) return e;
-  const long long persistent = (cus / 8) * 8;
-  dim3 grid((unsigned)(persistent >= 8 && total > persistent ? persistent : total)), block(kThreads);
+  // One workgroup per CU (a multiple of 8), or fewer for a small launch.
+  const long long persistent = cus >= 8 ? (cus / 8) * 8 : 8;
+  const long long need = (total + 7) / 8 * 8;
+  dim3 grid((unsigned)(need < persistent ? need : persistent)), block(kThreads);
   switch (role) {
     case kGram: hipLaunchKernelGGL(ns_gemm_bf16<kGram>, grid, block, 0, s, g); break;
     case kPoly: hipLaunchKernelGGL(ns_gemm_bf16<kPoly>, grid, block, 0, s, g); break;

@@ -43,6 +43,8 @@ struct MomentumArgs {
   void* x0;                 // workspace X0 of the batch
   size_t mat_x;             // elements per padded matrix
   float* partials;          // [batch matrices][ew_blocks]
+  int* nonzero;             // [batch matrices][ew_blocks]: 1 if any u of the tile is
+                            // not exactly 0 (NaN included), else 0
   int has_buf;              // 0: NS input is src itself (orthogonalize)
   float beta;               // buf' = beta*buf + kg*g
   float kg;                 // 1-beta (EMA) or 1 (heavy ball)
@@ -51,17 +53,29 @@ struct MomentumArgs {
 };
 
 // Norm finalize: scales[i] = 1 / (sqrt(sum_k partials[i][k]) + eps).
+// Compaction of the per-matrix live flags of a batch into the list of live
+// matrices (ascending) and its length, by one workgroup.
+hipError_t launch_compact(const int* live, int count, int* live_list, int* nlive, hipStream_t s);
+
 struct FinalizeArgs {
   int count;
   int ew_blocks;
   const float* partials;
   float* scales;
   float eps;
+  const int* nonzero;       // per-tile flags of the momentum pass
+  int* live;                // per matrix: 1 unless every u is exactly 0
 };
 
 // Apply pass: mode 0: p' = alpha*p - gamma[tr]*O; mode 1: out = O.
 // O is the wide workspace matrix, times scales[i] when use_scale.
 struct ApplyArgs {
+  // live (per batch matrix) or nullptr: O is taken as exactly 0 where
+  // live[i] == 0 (the NS iterate of those matrices is not stored);
+  // dead_only: matrices with live[i] != 0 are left alone (their apply runs
+  // inside the last Update GEMM).
+  const int* live;
+  int dead_only;
   int count;
   int m, n, n_pad;
   int first;
@@ -107,6 +121,12 @@ struct GemmArgs {
   // applied: p' = alpha*p - gamma[tr]*O (apply_mode 0) or out = O (1), O
   // being X' rounded to bf16, in the matrix's original orientation.
   const ApplyEntry* ptab;
+  // bf16 only: the matrices to compute, when not all of the batch: indices
+  // of the matrices whose NS input is not exactly zero (idle experts are
+  // left out: their iterate stays zero, so no product is needed), and
+  // their number (both in device memory). nullptr: every matrix.
+  const int* live_list;
+  const int* nlive;
   float alpha;
   float gamma[2];
   int apply_mode;

@@ -182,6 +182,13 @@ int run(const std::vector<MatRef>& mats, float lr, float beta, int ns_steps, muo
     void* Am = W + L.a;
     void* Bm = W + L.b;
     float* partials = reinterpret_cast<float*>(W + L.partials);
+    int* nonzero = reinterpret_cast<int*>(W + L.nonzero);
+    int* live = reinterpret_cast<int*>(W + L.live);
+    int* live_list = reinterpret_cast<int*>(W + L.live_list);
+    int* nlive = reinterpret_cast<int*>(W + L.nlive);
+    // bf16 with NS steps: matrices whose input is exactly zero (idle experts)
+    // get no GEMM work; their O is exactly 0.
+    const bool skip_zero = bf16 && ns_steps > 0;
     float* scales = reinterpret_cast<float*>(W + L.scales);
     ApplyEntry* ptab = reinterpret_cast<ApplyEntry*>(W + L.ptab);
     const double elems = (double)B.m * B.n;
@@ -207,7 +214,7 @@ int run(const std::vector<MatRef>& mats, float lr, float beta, int ns_steps, muo
       MomentumArgs a;
       a.count = cn; a.m = B.m; a.n = B.n; a.m_pad = B.m_pad; a.n_pad = B.n_pad;
       a.ew_blocks = L.ew_blocks; a.first = c0; a.x0 = x0; a.mat_x = L.mat_x;
-      a.partials = partials; a.has_buf = orthogonalize_only ? 0 : 1;
+      a.partials = partials; a.nonzero = nonzero; a.has_buf = orthogonalize_only ? 0 : 1;
       a.beta = beta; a.kg = kg; a.nesterov = o.nesterov;
       a.ptab = fused_apply ? ptab : nullptr;
       const double bytes = cn * elems * ((orthogonalize_only ? es : es + 4 + 4) + es);
@@ -219,10 +226,14 @@ int run(const std::vector<MatRef>& mats, float lr, float beta, int ns_steps, muo
 
     // 2. per-matrix Frobenius scale
     {
-      FinalizeArgs f{B.count, L.ew_blocks, partials, scales, o.eps};
+      FinalizeArgs f{B.count, L.ew_blocks, partials, scales, o.eps, nonzero, live};
       ProfScope ps("norm_finalize", 0.0, (double)B.count * L.ew_blocks * 4, stream);
       e = launch_finalize(f, stream);
       if (e != hipSuccess) { status = hip_fail(e, "finalize kernel launch"); break; }
+      if (skip_zero) {
+        e = launch_compact(live, B.count, live_list, nlive, stream);
+        if (e != hipSuccess) { status = hip_fail(e, "compact kernel launch"); break; }
+      }
     }
 
     // 3. NS iterations; the Frobenius scale is folded into the first step.
@@ -251,6 +262,8 @@ int run(const std::vector<MatRef>& mats, float lr, float beta, int ns_steps, muo
         g.out = r == 0 ? Am : (r == 1 ? Bm : Xn);
         g.scales = (k == 0 && r != 1) ? scales : nullptr;
         g.diag_add = r == 0 ? gram_diag : (r == 1 ? poly_diag : 0.0f);
+        g.live_list = skip_zero ? live_list : nullptr;
+        g.nlive = nlive;
         g.poly_operand = shifted ? 0 : 1;
         const bool apply_here = fused_apply && r == 2 && k + 1 == ns_steps;
         g.ptab = apply_here ? ptab : nullptr;
@@ -266,8 +279,11 @@ int run(const std::vector<MatRef>& mats, float lr, float beta, int ns_steps, muo
     }
     if (status) break;
 
-    // 4. apply (+ transpose back), unless the last Update did it
-    for (int c0 = 0; c0 < B.count && status == MUON_OK && !fused_apply; c0 += kEwChunk) {
+    // 4. apply (+ transpose back). With the apply fused into the last
+    // Update, only the skipped (zero-input) matrices remain, and only when
+    // their update p' = alpha*p (or out = 0) is not a no-op.
+    const bool dead_pass = fused_apply && (orthogonalize_only || apply_alpha != 1.0f);
+    for (int c0 = 0; c0 < B.count && status == MUON_OK && (!fused_apply || dead_pass); c0 += kEwChunk) {
       const int cn = std::min(kEwChunk, B.count - c0);
       EwMats em;
       std::memset(&em, 0, sizeof(em));
@@ -278,6 +294,8 @@ int run(const std::vector<MatRef>& mats, float lr, float beta, int ns_steps, muo
         em.tr[k] = r.rows > r.cols ? 1 : 0;
       }
       ApplyArgs a;
+      a.live = skip_zero ? live : nullptr;
+      a.dead_only = fused_apply ? 1 : 0;
       a.count = cn; a.m = B.m; a.n = B.n; a.n_pad = B.n_pad; a.first = c0;
       a.x = X; a.mat_x = L.mat_x; a.scales = scales; a.use_scale = ns_steps == 0 ? 1 : 0;
       a.mode = orthogonalize_only ? 1 : 0;

@@ -33,7 +33,11 @@ Layout batch_layout(int count, int m_pad, int n_pad, muon_dtype dtype) {
   L.a = off;        off = align_up(off + (size_t)count * L.mat_a * es, A);
   L.b = off;        off = align_up(off + (size_t)count * L.mat_a * es, A);
   L.partials = off; off = align_up(off + (size_t)count * (size_t)L.ew_blocks * sizeof(float), A);
+  L.nonzero = off;  off = align_up(off + (size_t)count * (size_t)L.ew_blocks * sizeof(int), A);
   L.scales = off;   off = align_up(off + (size_t)count * sizeof(float), A);
+  L.live = off;     off = align_up(off + (size_t)count * sizeof(int), A);
+  L.live_list = off; off = align_up(off + (size_t)count * sizeof(int), A);
+  L.nlive = off;    off = align_up(off + sizeof(int), A);
   L.ptab = off;     off = align_up(off + (size_t)count * 16, A);   // fused-apply entries
   L.total = off;
   return L;

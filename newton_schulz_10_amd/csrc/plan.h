@@ -38,7 +38,8 @@ struct Plan {
 
 // Byte offsets of one batch's workspace regions (each 512-byte aligned).
 struct Layout {
-  size_t x0 = 0, x1 = 0, a = 0, b = 0, partials = 0, scales = 0, ptab = 0, total = 0;
+  size_t x0 = 0, x1 = 0, a = 0, b = 0, partials = 0, nonzero = 0, scales = 0, live = 0, live_list = 0,
+         nlive = 0, ptab = 0, total = 0;
   size_t mat_x = 0;     // elements per padded m_pad x n_pad matrix
   size_t mat_a = 0;     // elements per padded m_pad x m_pad matrix
   int ew_blocks = 0;    // elementwise tiles per matrix

@@ -250,6 +250,23 @@ def test_zero_and_nan_matrices(nsa):
     assert check_update(case[0]["params"].as_f64(), from_device(P[0]), ref[0][0], "bf16", BF16_TOL) <= BF16_TOL
 
 
+def test_zero_matrices_with_weight_decay(nsa):
+    # Zero-gradient (idle) members skip the NS GEMMs on the bf16 path; their
+    # update is still the decay p' = (1 - lr*wd) p, bitwise as the general
+    # formula with O = 0 gives. Tall and wide members, a member whose shape
+    # takes the separate apply pass (300 x 130), and live members alongside.
+    shapes = [(256, 384), (384, 256), (256, 384), (384, 256), (300, 130), (130, 300)]
+    case = workloads.random_case(16, shapes, "bf16", momentum_init="zero", zero=(0, 3, 4))
+    p1, m1 = run_case(nsa, case, "bf16", 0.02, 0.95, 5, weight_decay=0.1)
+    ref = oracle_case(case, 0.02, 0.95, 5, weight_decay=0.1)
+    assert_parity(case, "bf16", p1, m1, ref, BF16_TOL)
+    alpha = np.float32(1.0 - float(np.float32(0.02)) * float(np.float32(0.1)))   # as the library forms it
+    for i in (0, 3, 4):
+        p0 = case[i]["params"].as_f64().astype(np.float32)
+        want = workloads._store(p0 * alpha, "bf16").as_f64()
+        assert np.array_equal(p1[i], want), i
+
+
 def test_non_default_stream(nsa):
     import torch
     case = workloads.random_case(12, [(256, 256)] * 2, "bf16")
