@@ -32,8 +32,8 @@ struct ApplyEntry {
 
 // Momentum pass: reads each matrix's source (and momentum buffer), writes
 // the buffer, the wide zero-padded NS input X0 = u (rounded to the
-// workspace type), optionally its transpose X0^T, and one fp32 partial sum
-// of u^2 per 64x64 tile.
+// workspace type), and per 64x64 tile one fp32 partial sum of u^2 and a
+// flag telling whether any u of the tile is nonzero.
 struct MomentumArgs {
   int count;                // matrices in this chunk
   int m, n;                 // wide shape (m <= n)
@@ -52,11 +52,12 @@ struct MomentumArgs {
   ApplyEntry* ptab;         // [batch matrices] entries to fill (dst, tr), or nullptr
 };
 
-// Norm finalize: scales[i] = 1 / (sqrt(sum_k partials[i][k]) + eps).
 // Compaction of the per-matrix live flags of a batch into the list of live
 // matrices (ascending) and its length, by one workgroup.
 hipError_t launch_compact(const int* live, int count, int* live_list, int* nlive, hipStream_t s);
 
+// Norm finalize: scales[i] = 1 / (sqrt(sum_k partials[i][k]) + eps), and
+// live[i] from the tile flags.
 struct FinalizeArgs {
   int count;
   int ew_blocks;
@@ -93,7 +94,9 @@ struct ApplyArgs {
 // tiles on one side of the diagonal and mirror them.
 //   fp32 kernels: Poly writes B = b*A + c*(A A), Update X' = sc*(a*X + B X).
 //   bf16 kernels: Poly writes B' = a*I + b*A + c*(A A), Update X' = sc*(B' X)
-//                 (the same product, with a*X moved into B').
+//                 (the same product, with a*X moved into B'); with c != 0,
+//                 Gram writes A' = A + (b/2c) I and Poly B' = c A'A' +
+//                 (a - b^2/4c) I, the same polynomial completed to a square.
 enum GemmRole {
   kGram = 0,    // A   = sc * X X^T                (sc = s_i^2 or 1)
   kPoly = 1,    // B   (A symmetric)
