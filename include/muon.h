@@ -106,9 +106,14 @@ typedef struct muon_options {
   int compute_units;      /* bf16: the balanced split of a shape group into
                              batches (same batch count or a few more, never over
                              the cap) is chosen so that the GEMM tiles fill whole
-                             rounds of this many compute units. -1 (default): the
-                             current device's count (no fitting when no device
-                             is visible); 0: no fitting (fewest batches).      */
+                             rounds of this many compute units, counting every
+                             matrix as computed. 0 (default): no fitting (fewest
+                             batches); -1: the current device's count (no
+                             fitting when no device is visible). Matrices whose
+                             NS input is exactly zero are skipped on the device,
+                             so when some are, a fitted split can leave a
+                             nearly empty last round: fit only groups that are
+                             known to have none.                              */
 } muon_options;
 
 /* Fills *opts with the defaults above. */

@@ -135,7 +135,7 @@ def _matrices(t: torch.Tensor, what: str) -> List[Tuple[int, int, int]]:
 
 
 def _options(nesterov=True, momentum_form="ema", weight_decay=0.0, scale_rule="rms", rms_target=0.2,
-             eps=1e-7, coeffs=None, batch_cap_elems=0, compute_units=-1, ns_steps=5):
+             eps=1e-7, coeffs=None, batch_cap_elems=0, compute_units=0, ns_steps=5):
     o = Options()
     load().muon_default_options(ctypes.byref(o))
     o.nesterov = 1 if nesterov else 0
@@ -216,7 +216,7 @@ def muon_step(mats: Iterable[Tuple[torch.Tensor, torch.Tensor, torch.Tensor]], l
 
 def muon_orthogonalize(inputs: Sequence[torch.Tensor], outputs: Sequence[torch.Tensor], ns_steps: int = 5,
                        stream=None, eps: float = 1e-7, coeffs=None, batch_cap_elems: int = 0,
-                       compute_units: int = -1) -> None:
+                       compute_units: int = 0) -> None:
     """C `muon_orthogonalize`: outputs[i] = NS(inputs[i]) (same shapes)."""
     I = [x for t in inputs for x in _matrices(t, "inputs")]
     O = [x for t in outputs for x in _matrices(t, "outputs")]
@@ -237,7 +237,7 @@ def muon_orthogonalize(inputs: Sequence[torch.Tensor], outputs: Sequence[torch.T
 
 
 def plan_query(shapes: Sequence[Tuple[int, int]], dtype: torch.dtype = torch.bfloat16,
-               batch_cap_elems: int = 0, compute_units: int = -1) -> dict:
+               batch_cap_elems: int = 0, compute_units: int = 0) -> dict:
     """C `muon_plan_query` (host only): the batches and order muon_step would use."""
     L = load()
     n = len(shapes)

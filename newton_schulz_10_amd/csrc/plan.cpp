@@ -149,7 +149,7 @@ void default_options(muon_options& o) {
   o.eps = 1e-7f;
   o.coeffs = nullptr;
   o.batch_cap_elems = MUON_DEFAULT_BATCH_CAP;
-  o.compute_units = -1;
+  o.compute_units = 0;
 }
 
 int check_options(const muon_options& o, int ns_steps, std::string& err) {

@@ -91,6 +91,10 @@ def test_plan_query_moe_bank(lib):
     assert fitted["order"] == list(range(512))
     with pytest.raises(nsa.MuonError):
         nsa.plan_query(shapes, torch.bfloat16, compute_units=-2)
+    # The default does not fit (idle matrices are skipped on the device, so a
+    # split fitted for all of them can leave a nearly empty last round).
+    assert [b["count"] for b in nsa.plan_query(shapes, torch.bfloat16)["batches"]] == [171, 171, 170]
+    nsa.plan_query(shapes, torch.bfloat16, compute_units=-1)   # current device, or none: accepted
 
 
 def test_plan_query_mlp_and_stack(lib):
