@@ -642,6 +642,240 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& g, int mat, int I, int
   }
 }
 
+// Diagonal tile of A'/B' (I == J, full, no epilogue operand). The block is
+// symmetric and its P and Q rows are the same 256 rows, so those are staged
+// once, and only the 36 of its 64 blocks of 32 x 32 on or below the
+// diagonal are multiplied:
+//   waves 0 and 3: the lower triangles of the two diagonal quadrants (rows
+//                  and columns 0-127, resp. 128-255): 10 blocks each;
+//   waves 1 and 2: rows 128-255 x columns 0-63, resp. 64-127: 8 blocks.
+// The 28 blocks above the diagonal are the transposes of blocks below it,
+// element for element as the products are (the MFMA multiplies exactly
+// and sums in the same k order), copied in LDS before the tile is stored.
+// Kind 0 (triangle): MFMA i of a step multiplies column fragment
+// diag_a(0, i) by row fragment diag_b(0, i), over the pairs b >= a; kind 1
+// (rectangle): 2 column x 4 row fragments.
+__device__ constexpr int diag_nm(int kind) { return kind == 0 ? 10 : 8; }   // MFMAs per step
+__device__ constexpr int diag_nr(int kind) { return kind == 0 ? 8 : 6; }    // fragments per step
+__device__ constexpr int diag_a(int kind, int i) {
+  return kind == 0 ? (i < 4 ? 0 : i < 7 ? 1 : i < 9 ? 2 : 3) : (i < 4 ? 0 : 1);
+}
+__device__ constexpr int diag_b(int kind, int i) {
+  return kind == 0 ? (i < 4 ? i : i < 7 ? i - 3 : i < 9 ? i - 5 : 3) : (i & 3);
+}
+// Column block C of upper pair p (pairs enumerate C = 1..7, R = 0..C-1).
+__device__ constexpr int upper_c(int p) {
+  return p < 1 ? 1 : p < 3 ? 2 : p < 6 ? 3 : p < 10 ? 4 : p < 15 ? 5 : p < 21 ? 6 : 7;
+}
+
+template <int ROLE>
+__device__ __forceinline__ void gemm_diag_tile(const GemmArgs& g, int mat, int I, Stages& lds) {
+  static_assert(ROLE != kUpdate, "symmetric roles only");
+  constexpr int NL = 4;     // 1 KiB fill loads per wave per slab: 256 rows of 64 B over 4 waves
+  constexpr int NLh = NL / 2;
+  constexpr int QR = TILE;
+  const int K = (ROLE == kGram) ? g.n_pad : g.m_pad;
+  const bf16_t* P = (ROLE == kGram) ? static_cast<const bf16_t*>(g.x) + (size_t)mat * g.mat_x
+                                    : static_cast<const bf16_t*>(g.a) + (size_t)mat * g.mat_a;
+  P += (size_t)(I * TILE) * K;
+
+  int tid = threadIdx.x;
+  asm volatile("" : "+v"(tid));
+  const int lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int nk = K / BK;
+  const int last = nk - 1;
+  // Stage rows 0-255 hold the tile's 256 rows ([row][32 k], chunks swizzled
+  // by kswz); load q of a wave fills rows (4q + wave)*16 .. +15.
+  auto fill_one = [&](int kt, int q) {
+    const int k0 = (kt < last ? kt : last) * BK;   // past the end: repeat the last slab
+    const int rb = (q * 4 + wave) * 16;
+    const int r = rb + (lane >> 2);
+    dma16(P + (size_t)r * K + k0 + ((lane & 3) ^ kswz(r)) * 8, &lds[kt & (kStages - 1)][rb * BK]);
+  };
+  for (int j = 0; j < kStages - 1; ++j)
+    for (int q = 0; q < NL; ++q) fill_one(j, q);
+  __builtin_amdgcn_s_waitcnt(vmcnt(2 * NL));  // fill(0) landed
+  lds_barrier();
+
+  float sc = 1.0f;
+  if (g.scales) {
+    const float sv = g.scales[mat];
+    sc = (ROLE == kGram) ? sv * sv : sv;
+  }
+  bf16_t* T = &lds[0][0];
+  const bool dgon = g.diag_add != 0.0f;
+
+  // Main loop and fp32 epilogue of one wave kind. Same pipeline as the
+  // general tile (fills three slabs ahead, one barrier per slab, fragments
+  // double buffered); after MFMA i a hook issues the next step's fragment
+  // read i (i < NR), then the step's fill loads.
+  auto run = [&](auto kind_c, int rbase, int cbase) {
+    constexpr int KIND = decltype(kind_c)::value;
+    constexpr int NM = diag_nm(KIND), NR = diag_nr(KIND);
+    // Fragment f in first-use order: rf0, cf0, rf1, rf2, rf3, cf1, cf2, cf3.
+    auto read_one = [&](int kt, int ks, int f, bf16x8 (&rf)[4], bf16x8 (&cf)[4]) {
+      const bf16_t* S = lds[kt & (kStages - 1)];
+      const int ch = 2 * ks + (lane >> 5);
+      const bool is_c = (f == 1 || f >= 5);
+      const int idx = (f == 0 || f == 1) ? 0 : (f <= 4 ? f - 1 : f - 4);
+      const int r = (is_c ? cbase : rbase) + idx * 32 + (lane & 31);
+      const bf16x8 v = *reinterpret_cast<const bf16x8*>(S + r * BK + ((ch ^ kswz(r)) * 8));
+      if (is_c) cf[idx] = v; else rf[idx] = v;
+    };
+    f32x16 acc[4][4];
+#pragma unroll
+    for (int a = 0; a < 4; ++a)
+#pragma unroll
+      for (int b = 0; b < 4; ++b)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) acc[a][b][v] = 0.0f;
+    bf16x8 rf[2][4], cf[2][4];
+#pragma unroll
+    for (int f = 0; f < NR; ++f) read_one(0, 0, f, rf[0], cf[0]);
+    auto mstep = [&](int cur, auto hook) {
+#pragma unroll
+      for (int i = 0; i < NM; ++i) {
+        const int a = diag_a(KIND, i), b = diag_b(KIND, i);
+        acc[a][b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(cf[cur][a], rf[cur][b], acc[a][b], 0, 0, 0);
+        __builtin_amdgcn_sched_barrier(0);
+        hook(i);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    };
+    auto fill_slot = [&](int kt, int h, int i) {
+#pragma unroll
+      for (int q = 0; q < NLh; ++q)
+        if (NR + q == i) fill_one(kt, h * NLh + q);
+    };
+    auto slab = [&](int kt, auto more) {
+      if constexpr (decltype(more)::value) {
+        mstep(0, [&](int i) {
+          if (i < NR) read_one(kt, 1, i, rf[1], cf[1]);
+          fill_slot(kt + 3, 0, i);
+        });
+        __builtin_amdgcn_s_waitcnt(vmcnt_lgkm0(NL + NLh));
+        lds_barrier();
+        mstep(1, [&](int i) {
+          if (i < NR) read_one(kt + 1, 0, i, rf[0], cf[0]);
+          fill_slot(kt + 3, 1, i);
+        });
+      } else {
+        mstep(0, [&](int i) {
+          if (i < NR) read_one(kt, 1, i, rf[1], cf[1]);
+        });
+        mstep(1, [](int) {});
+      }
+    };
+    for (int kt = 0; kt < last; ++kt) slab(kt, std::true_type{});
+    slab(last, std::false_type{});
+
+    __builtin_amdgcn_s_waitcnt(0x0070);  // vmcnt(0) lgkmcnt(0): stages no longer read
+    lds_barrier();
+
+    // fp32 form, rounded once to bf16 into T (rows of 256, chunks swizzled
+    // by eswz): Gram A' = sc * acc + d I, Poly B' = c acc + d I. acc[a][b]
+    // element v: row rbase + 32b + lane%32, columns cbase + 32a + 8*(v/4) +
+    // 4*(lane/32) + v%4; on a block with a == b of kind 0 the diagonal is
+    // element 4*(l/8) + l%4 (l = lane % 32) of the lanes with lane/32 ==
+    // (l/4) % 2.
+    int etid = threadIdx.x;
+    asm volatile("" : "+v"(etid));
+    const int el = etid & 63, l32 = el & 31;
+    const int dsel = (KIND == 0 && (el >> 5) == ((l32 >> 2) & 1)) ? 4 * (l32 >> 3) + (l32 & 3) : -1;
+#pragma unroll
+    for (int i = 0; i < NM; ++i) {
+      const int a = diag_a(KIND, i), b = diag_b(KIND, i);
+      const int row_i = rbase + b * 32 + l32;
+      bf16_t* row = T + row_i * QR;
+      const int sw = eswz(row_i);
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        float v[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          v[e] = acc[a][b][4 * q + e];
+          v[e] = (ROLE == kPoly) ? v[e] * g.cc : v[e] * sc;
+          if (KIND == 0 && a == b && dgon) v[e] += (4 * q + e == dsel) ? g.diag_add : 0.0f;
+        }
+        const int j = cbase + a * 32 + 8 * q + 4 * (el >> 5);
+        uint2 o;
+        o.x = f32x2_to_bf16x2(v[0], v[1]);
+        o.y = f32x2_to_bf16x2(v[2], v[3]);
+        *reinterpret_cast<uint2*>(row + (((j >> 3) ^ sw) << 3) + (j & 7)) = o;
+      }
+    }
+  };
+  if (wave == 0 || wave == 3) {
+    const int qb = wave == 0 ? 0 : 128;
+    run(std::integral_constant<int, 0>{}, qb, qb);
+  } else {
+    run(std::integral_constant<int, 1>{}, 128, wave == 1 ? 0 : 64);
+  }
+  __syncthreads();
+
+  int etid = threadIdx.x;
+  asm volatile("" : "+v"(etid));
+  const int etid2 = etid, el = etid & 63;
+  const int grp = el >> 4, jj = el & 15;
+  auto tidx = [&](int i, int j) { return i * QR + (((j >> 3) ^ eswz(i)) << 3) + (j & 7); };
+  // Transposing gather: lane (grp, jj) receives column c0 + jj of rows
+  // i0 + 8*grp .. +7 (two ds_read_b64_tr_b16 of 4 rows each).
+  auto tr8 = [&](int i0, int c0) {
+    s16x4 h[2];
+#pragma unroll
+    for (int half = 0; half < 2; ++half) {
+      const int row = i0 + 8 * grp + 4 * half + (jj >> 2);
+      h[half] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(T + tidx(row, c0 + 4 * (jj & 3))));
+    }
+    return __builtin_bit_cast(uint4, __builtin_shufflevector(h[0], h[1], 0, 1, 2, 3, 4, 5, 6, 7));
+  };
+  // Upper blocks (R, C), R < C, from lower blocks (C, R): 28 pairs x two
+  // 16-column halves = 56 gathers, 14 per wave: gather u of wave w takes
+  // pair 2u + w/2, half w%2; pair p enumerates C = 1..7, R = 0..C-1.
+  {
+    constexpr int NU = 14;
+    uint4 v[NU];
+    int dst[NU];
+    const int w1 = wave >> 1, hh = wave & 1;
+#pragma unroll
+    for (int u = 0; u < NU; ++u) {
+      const int C = w1 ? upper_c(2 * u + 1) : upper_c(2 * u);
+      const int R = (w1 ? 2 * u + 1 : 2 * u) - C * (C - 1) / 2;
+      const int i0 = C * 32, c0 = R * 32 + 16 * hh;
+      v[u] = tr8(i0, c0);
+      dst[u] = tidx(c0 + jj, i0 + 8 * grp);
+    }
+    keep_batch(v);
+#pragma unroll
+    for (int u = 0; u < NU; ++u) *reinterpret_cast<uint4*>(T + dst[u]) = v[u];
+  }
+  __syncthreads();
+
+  // Tile rows -> out, 16 B per lane, 32 lanes per row, reads in batches of
+  // 8 ahead of their stores.
+  const int ldo = g.m_pad;
+  bf16_t* const otile = static_cast<bf16_t*>(g.out) + (size_t)mat * g.mat_a + (size_t)(I * TILE) * ldo + I * TILE;
+  constexpr int TC8 = QR / 8;
+  constexpr int kBatch = 8;
+#pragma unroll
+  for (int r0 = 0; r0 < (TILE * TC8) / kThreads; r0 += kBatch) {
+    uint4 v[kBatch];
+#pragma unroll
+    for (int u = 0; u < kBatch; ++u) {
+      const int id = (r0 + u) * kThreads + etid2;
+      const int i = id / TC8, c = id % TC8;
+      v[u] = *reinterpret_cast<const uint4*>(T + i * QR + ((c ^ eswz(i)) << 3));
+    }
+    keep_batch(v);
+#pragma unroll
+    for (int u = 0; u < kBatch; ++u) {
+      const int id = (r0 + u) * kThreads + etid2;
+      const int i = id / TC8, c = id % TC8;
+      store16_at(otile, i * ldo + c * 8, v[u]);
+    }
+  }
+}
+
 // One grid covers every tile of every computed matrix of the batch: at
 // most one workgroup per CU, a multiple of 8, each looping over the tiles
 // of its XCD's contiguous range (slot s taking tiles s, s + slots, ...), so
@@ -683,7 +917,12 @@ void ns_gemm_bf16(GemmArgs g) {
         I = u / G.tn;
         J = u % G.tn;
       }
-      gemm_tile<ROLE, false>(g, mat, I, J, lds);
+      if constexpr (kSym) {
+        if (I == J && !(ROLE == kPoly && g.poly_operand)) gemm_diag_tile<ROLE>(g, mat, I, lds);
+        else gemm_tile<ROLE, false>(g, mat, I, J, lds);
+      } else {
+        gemm_tile<ROLE, false>(g, mat, I, J, lds);
+      }
     } else {
       gemm_tile<ROLE, true>(g, mat, G.F, 2 * (u - G.full), lds);
     }
