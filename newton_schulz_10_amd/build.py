@@ -37,6 +37,10 @@ def common_flags():
             f"--offload-arch={ARCH}",
             # Packed fp32 VALU forms are kept out of the generated code.
             "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+            # Atomics stay single instructions: the GEMM's tile claim (one
+            # lane) must not be rewritten into a wave reduction that uses
+            # its result, and so waits for it, right away.
+            "-mllvm", "-amdgpu-atomic-optimizer-strategy=None",
             "-I", INCLUDE, "-I", CSRC]
 
 

@@ -372,9 +372,11 @@ __global__ __launch_bounds__(256) void apply_kernel(EwMats mats, ApplyArgs a) {
 
 // One workgroup: the live flags of a batch -> the ascending list of live
 // matrices and its length (a block-wide scan of per-thread counts).
-__global__ __launch_bounds__(256) void compact_kernel(const int* live, int count, int* list, int* nlive) {
+__global__ __launch_bounds__(256) void compact_kernel(const int* live, int count, int* list, int* nlive,
+                                                     int* sched) {
   __shared__ int sums[256];
   const int t = threadIdx.x;
+  if (sched && t < 16) sched[t] = 0;
   const int per = (count + 255) / 256;
   const int lo = t * per, hi = min(count, lo + per);
   int c = 0;
@@ -395,9 +397,9 @@ __global__ __launch_bounds__(256) void compact_kernel(const int* live, int count
 
 }  // namespace
 
-hipError_t launch_compact(const int* live, int count, int* live_list, int* nlive, hipStream_t s) {
+hipError_t launch_compact(const int* live, int count, int* live_list, int* nlive, int* sched, hipStream_t s) {
   if (count <= 0) return hipSuccess;
-  hipLaunchKernelGGL(compact_kernel, dim3(1), dim3(256), 0, s, live, count, live_list, nlive);
+  hipLaunchKernelGGL(compact_kernel, dim3(1), dim3(256), 0, s, live, count, live_list, nlive, sched);
   return hipGetLastError();
 }
 

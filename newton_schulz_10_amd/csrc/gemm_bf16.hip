@@ -54,6 +54,7 @@
 
 #include "device_common.h"
 #include "kernels.h"
+#include "plan.h"
 
 namespace muon {
 
@@ -98,8 +99,11 @@ __device__ __forceinline__ int eswz(int i) { return (i & 31) ^ ((i >> 5) & 7); }
 // conservative LDS-DMA alias tracking would otherwise wait for the fills of
 // later slabs before any LDS read); completion is awaited with explicit
 // vmcnt waits. `lds_dst` must be wave-uniform.
+// A flat address of LDS is the shared aperture (high 32 bits) with the LDS
+// byte address in the low 32 bits: truncating gives the LDS address (no
+// null check, which an address-space cast would add).
 __device__ __forceinline__ unsigned lds_addr(const void* p) {
-  return static_cast<unsigned>(reinterpret_cast<uintptr_t>((const __attribute__((address_space(3))) char*)(p)));
+  return static_cast<unsigned>(reinterpret_cast<uintptr_t>(p));
 }
 __device__ __forceinline__ void dma16(const void* g, const void* lds_dst) {
   asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, off"
@@ -136,6 +140,35 @@ constexpr int vmcnt_lgkm0(int n) { return ((n >> 4) << 14) | (n & 15) | 0x0070; 
 
 typedef bf16_t Stages[kStages][kStageRows * BK];
 
+// Dynamic tile claim of the persistent loop (see ns_gemm_bf16). Thread 0
+// claims the next tile (an atomic on the XCD's counter) when the last
+// K-slab of the current one starts: that slab issues no loads, so no wait
+// in it covers the atomic. The claim is published through the workgroup's
+// slot before the barrier that follows the fp32 epilogue form, read back by
+// every thread after it and first used when the tile is done, so neither
+// latency delays the tile.
+struct Claim {
+  int* ctr;    // the XCD's tile counter, or nullptr (static schedule)
+  int* slot;   // the workgroup's broadcast slot
+  int first;   // tile of counter value 0
+  int end;     // end of the XCD's tile range
+};
+__device__ __forceinline__ int claim_issue(const Claim& c, int tid) {
+  int v = 0;
+  if (c.ctr && tid == 0) v = atomicAdd(c.ctr, 1);
+  return v;
+}
+__device__ __forceinline__ void claim_publish(const Claim& c, int tid, int claim) {
+  if (c.ctr && tid == 0) {
+    // A claim past the range (or any value outside it) ends the loop.
+    const int next = (claim >= 0 && claim < c.end - c.first) ? c.first + claim : c.end;
+    __hip_atomic_store(c.slot, next, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
+}
+__device__ __forceinline__ int claim_load(const Claim& c) {
+  return c.ctr ? __hip_atomic_load(c.slot, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) : 0;
+}
+
 // Tile geometry of one batch: F full tile rows of 256 (rows of A/B and X),
 // plus one half row of 128 when m_pad is an odd multiple of 128, covered by
 // wide tiles. Per matrix: `full` tiles, then `wide` tiles.
@@ -160,7 +193,8 @@ __device__ __forceinline__ Geom geom(const GemmArgs& g, bool sym) {
 // computed from clamped loads and never stored. `lds`: the K-slab stages,
 // reused as the epilogue tile.
 template <int ROLE, bool WIDE>
-__device__ __forceinline__ void gemm_tile(const GemmArgs& g, int mat, int I, int J, Stages& lds) {
+__device__ __forceinline__ void gemm_tile(const GemmArgs& g, int mat, int I, int J, Stages& lds,
+                                          const Claim& cl, int& next) {
   constexpr bool kSym = (ROLE != kUpdate);
   constexpr int PR = WIDE ? 128 : 256;   // tile rows (P rows)
   constexpr int QR = WIDE ? 512 : 256;   // tile columns (Q rows)
@@ -347,6 +381,7 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& g, int mat, int I, int
     }
   };
   for (int kt = 0; kt < last; ++kt) slab(kt, std::true_type{});
+  const int claim = claim_issue(cl, tid);
   slab(last, std::false_type{});
 
   // ---- epilogue ----------------------------------------------------------
@@ -488,7 +523,9 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& g, int mat, int I, int
   } else {
     if (g.scales) form(F0{}, T1{}, F0{}); else form(F0{}, F0{}, F0{});
   }
+  claim_publish(cl, tid, claim);
   __syncthreads();
+  next = claim_load(cl);
 
   // A diagonal block needs no symmetrizing: element (i, j) and (j, i) are
   // the same products (the MFMA multiplies exactly; a*b = b*a) summed in the
@@ -669,7 +706,8 @@ __device__ constexpr int upper_c(int p) {
 }
 
 template <int ROLE>
-__device__ __forceinline__ void gemm_diag_tile(const GemmArgs& g, int mat, int I, Stages& lds) {
+__device__ __forceinline__ void gemm_diag_tile(const GemmArgs& g, int mat, int I, Stages& lds,
+                                               const Claim& cl, int& next) {
   static_assert(ROLE != kUpdate, "symmetric roles only");
   constexpr int NL = 4;     // 1 KiB fill loads per wave per slab: 256 rows of 64 B over 4 waves
   constexpr int NLh = NL / 2;
@@ -704,6 +742,7 @@ __device__ __forceinline__ void gemm_diag_tile(const GemmArgs& g, int mat, int I
   }
   bf16_t* T = &lds[0][0];
   const bool dgon = g.diag_add != 0.0f;
+  int claim = 0;
 
   // Main loop and fp32 epilogue of one wave kind. Same pipeline as the
   // general tile (fills three slabs ahead, one barrier per slab, fragments
@@ -767,6 +806,7 @@ __device__ __forceinline__ void gemm_diag_tile(const GemmArgs& g, int mat, int I
       }
     };
     for (int kt = 0; kt < last; ++kt) slab(kt, std::true_type{});
+    claim = claim_issue(cl, tid);
     slab(last, std::false_type{});
 
     __builtin_amdgcn_s_waitcnt(0x0070);  // vmcnt(0) lgkmcnt(0): stages no longer read
@@ -811,7 +851,9 @@ __device__ __forceinline__ void gemm_diag_tile(const GemmArgs& g, int mat, int I
   } else {
     run(std::integral_constant<int, 1>{}, 128, wave == 1 ? 0 : 64);
   }
+  claim_publish(cl, tid, claim);
   __syncthreads();
+  next = claim_load(cl);
 
   int etid = threadIdx.x;
   asm volatile("" : "+v"(etid));
@@ -878,8 +920,11 @@ __device__ __forceinline__ void gemm_diag_tile(const GemmArgs& g, int mat, int I
 
 // One grid covers every tile of every computed matrix of the batch: at
 // most one workgroup per CU, a multiple of 8, each looping over the tiles
-// of its XCD's contiguous range (slot s taking tiles s, s + slots, ...), so
-// each XCD's L2 serves whole matrices.
+// of its XCD's contiguous range, so each XCD's L2 serves whole matrices.
+// Slot s of an XCD starts with tile s of the range; with the dynamic
+// schedule (g.sched) it then claims the next unclaimed tile of the range
+// from the XCD's counter (tiles differ in cost: diagonal tiles of A'/B'
+// multiply 36 of 64 blocks), else it takes tiles s + slots, s + 2 slots, ....
 // Tile order within a matrix: full tiles (row-major over the lower triangle
 // for A/B, over all rows x columns for X'), then the wide tiles of the
 // half row.
@@ -903,8 +948,13 @@ void ns_gemm_bf16(GemmArgs g) {
   int t = xcd * base + (xcd < rem ? xcd : rem) + slot;
   const int t_end = xcd * base + (xcd < rem ? xcd : rem) + base + (xcd < rem ? 1 : 0);
   const int step = gridDim.x / kXcd;
+  const int lo = xcd * base + (xcd < rem ? xcd : rem);
+  int* const sched = g.sched;
+  // Slot s starts with range tile s; counter value c means tile step + c.
+  const Claim cl{sched ? &sched[xcd] : nullptr, sched ? &sched[16 + blockIdx.x] : nullptr, lo + step, t_end};
 #pragma nounroll
-  for (; t < t_end; t += step) {
+  while (t < t_end) {
+    int next = 0;
     const int mat = g.live_list ? g.live_list[t / G.per_mat] : t / G.per_mat;
     const int u = t % G.per_mat;
     if (u < G.full) {
@@ -918,15 +968,25 @@ void ns_gemm_bf16(GemmArgs g) {
         J = u % G.tn;
       }
       if constexpr (kSym) {
-        if (I == J && !(ROLE == kPoly && g.poly_operand)) gemm_diag_tile<ROLE>(g, mat, I, lds);
-        else gemm_tile<ROLE, false>(g, mat, I, J, lds);
+        if (I == J && !(ROLE == kPoly && g.poly_operand)) gemm_diag_tile<ROLE>(g, mat, I, lds, cl, next);
+        else gemm_tile<ROLE, false>(g, mat, I, J, lds, cl, next);
       } else {
-        gemm_tile<ROLE, false>(g, mat, I, J, lds);
+        gemm_tile<ROLE, false>(g, mat, I, J, lds, cl, next);
       }
     } else {
-      gemm_tile<ROLE, true>(g, mat, G.F, 2 * (u - G.full), lds);
+      gemm_tile<ROLE, true>(g, mat, G.F, 2 * (u - G.full), lds, cl, next);
     }
     __syncthreads();   // the epilogue's LDS reads are done before the next fills
+    // Dynamic schedule: the tile claimed during the epilogue (thread 0's
+    // atomic, passed on through the workgroup's slot in global memory, as
+    // the stages take all of the LDS).
+    t = sched ? __builtin_amdgcn_readfirstlane(next) : t + step;
+  }
+  if (sched && threadIdx.x == 0) {
+    // Every workgroup has claimed its last tile: the last one to get here
+    // leaves the counters zeroed for the next launch on this workspace.
+    if (atomicAdd(&sched[8], 1) == (int)gridDim.x - 1)
+      for (int i = 0; i < 9; ++i) __hip_atomic_store(&sched[i], 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
 }
 
@@ -972,6 +1032,11 @@ hipError_t launch_gemm_bf16(GemmRole role, const GemmArgs& g, hipStream_t s) {
   const long long persistent = cus >= 8 ? (cus / 8) * 8 : 8;
   const long long need = (total + 7) / 8 * 8;
   dim3 grid((unsigned)(need < persistent ? need : persistent)), block(kThreads);
+  if (g.sched && grid.x > (unsigned)kSchedSlots) {   // more workgroups than broadcast slots
+    GemmArgs gs = g;
+    gs.sched = nullptr;
+    return launch_gemm_bf16(role, gs, s);
+  }
   switch (role) {
     case kGram: hipLaunchKernelGGL(ns_gemm_bf16<kGram>, grid, block, 0, s, g); break;
     case kPoly: hipLaunchKernelGGL(ns_gemm_bf16<kPoly>, grid, block, 0, s, g); break;

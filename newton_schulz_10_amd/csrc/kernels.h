@@ -54,7 +54,8 @@ struct MomentumArgs {
 
 // Compaction of the per-matrix live flags of a batch into the list of live
 // matrices (ascending) and its length, by one workgroup.
-hipError_t launch_compact(const int* live, int count, int* live_list, int* nlive, hipStream_t s);
+// It also zeroes the batch's GEMM tile scheduler counters (sched[0..15]).
+hipError_t launch_compact(const int* live, int count, int* live_list, int* nlive, int* sched, hipStream_t s);
 
 // Norm finalize: scales[i] = 1 / (sqrt(sum_k partials[i][k]) + eps), and
 // live[i] from the tile flags.
@@ -130,6 +131,12 @@ struct GemmArgs {
   // their number (both in device memory). nullptr: every matrix.
   const int* live_list;
   const int* nlive;
+  // bf16 only: tile scheduler words (see kSchedWords), or nullptr for the
+  // static schedule. sched[x], x < 8, counts the tiles claimed from XCD
+  // x's range, sched[8] the workgroups done; both are zero at launch (the
+  // last workgroup to finish zeroes them again); sched[16 + b] carries
+  // workgroup b's claimed tile to its waves.
+  int* sched;
   float alpha;
   float gamma[2];
   int apply_mode;

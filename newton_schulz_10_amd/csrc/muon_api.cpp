@@ -186,6 +186,7 @@ int run(const std::vector<MatRef>& mats, float lr, float beta, int ns_steps, muo
     int* live = reinterpret_cast<int*>(W + L.live);
     int* live_list = reinterpret_cast<int*>(W + L.live_list);
     int* nlive = reinterpret_cast<int*>(W + L.nlive);
+    int* sched = reinterpret_cast<int*>(W + L.sched);
     // bf16 with NS steps: matrices whose input is exactly zero (idle experts)
     // get no GEMM work; their O is exactly 0.
     const bool skip_zero = bf16 && ns_steps > 0;
@@ -231,7 +232,7 @@ int run(const std::vector<MatRef>& mats, float lr, float beta, int ns_steps, muo
       e = launch_finalize(f, stream);
       if (e != hipSuccess) { status = hip_fail(e, "finalize kernel launch"); break; }
       if (skip_zero) {
-        e = launch_compact(live, B.count, live_list, nlive, stream);
+        e = launch_compact(live, B.count, live_list, nlive, sched, stream);
         if (e != hipSuccess) { status = hip_fail(e, "compact kernel launch"); break; }
       }
     }
@@ -264,6 +265,12 @@ int run(const std::vector<MatRef>& mats, float lr, float beta, int ns_steps, muo
         g.diag_add = r == 0 ? gram_diag : (r == 1 ? poly_diag : 0.0f);
         g.live_list = skip_zero ? live_list : nullptr;
         g.nlive = nlive;
+        // Dynamic tile schedule for Gram (its diagonal tiles multiply 36 of
+        // 64 blocks, and K = n makes its tiles long); measured on the MoE
+        // bank it is 2.8% faster there and 0.6% / 1.3% slower for Poly and
+        // Update, whose tiles are shorter or all alike. The counters are
+        // zeroed by the compact kernel.
+        g.sched = (skip_zero && r == 0) ? sched : nullptr;
         g.poly_operand = shifted ? 0 : 1;
         const bool apply_here = fused_apply && r == 2 && k + 1 == ns_steps;
         g.ptab = apply_here ? ptab : nullptr;

@@ -39,6 +39,7 @@ Layout batch_layout(int count, int m_pad, int n_pad, muon_dtype dtype) {
   L.live_list = off; off = align_up(off + (size_t)count * sizeof(int), A);
   L.nlive = off;    off = align_up(off + sizeof(int), A);
   L.ptab = off;     off = align_up(off + (size_t)count * 16, A);   // fused-apply entries
+  L.sched = off;    off = align_up(off + (size_t)kSchedWords * sizeof(int), A);
   L.total = off;
   return L;
 }

@@ -19,6 +19,11 @@ namespace muon {
 
 // Element tile of the momentum/apply passes (wide orientation).
 constexpr int kEwTile = 64;
+// bf16 GEMM tile scheduler words per batch: 8 per-XCD tile counters, one
+// completion counter, padding to 16, then one broadcast slot per workgroup
+// (at most kSchedSlots workgroups use the dynamic schedule).
+constexpr int kSchedSlots = 1024;
+constexpr int kSchedWords = 16 + kSchedSlots;
 
 // One fused batch; m <= n is the group's wide shape.
 struct Batch {
@@ -39,7 +44,7 @@ struct Plan {
 // Byte offsets of one batch's workspace regions (each 512-byte aligned).
 struct Layout {
   size_t x0 = 0, x1 = 0, a = 0, b = 0, partials = 0, nonzero = 0, scales = 0, live = 0, live_list = 0,
-         nlive = 0, ptab = 0, total = 0;
+         nlive = 0, ptab = 0, sched = 0, total = 0;
   size_t mat_x = 0;     // elements per padded m_pad x n_pad matrix
   size_t mat_a = 0;     // elements per padded m_pad x m_pad matrix
   int ew_blocks = 0;    // elementwise tiles per matrix
