@@ -43,13 +43,19 @@ __device__ __forceinline__ void load4(const ST* p, int valid, float v[4]) {
 }
 
 // 4 whole elements at a 4-element-aligned address (interior tiles).
+// Aligned 4-element accesses of the interior tiles. Non-temporal: every
+// byte of these passes is touched once (the workspace of a batch is far
+// larger than the L2), and streaming hints measured 4% faster for the
+// momentum pass.
+typedef float nt_f32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned nt_u32x2 __attribute__((ext_vector_type(2)));
 template <typename ST>
 __device__ __forceinline__ void load4a(const ST* p, float v[4]) {
   if constexpr (sizeof(ST) == 4) {
-    const float4 q = *reinterpret_cast<const float4*>(p);
+    const nt_f32x4 q = __builtin_nontemporal_load(reinterpret_cast<const nt_f32x4*>(p));
     v[0] = q.x; v[1] = q.y; v[2] = q.z; v[3] = q.w;
   } else {
-    const uint2 q = *reinterpret_cast<const uint2*>(p);
+    const nt_u32x2 q = __builtin_nontemporal_load(reinterpret_cast<const nt_u32x2*>(p));
     v[0] = bf16_to_f32(q.x & 0xffffu); v[1] = bf16_to_f32(q.x >> 16);
     v[2] = bf16_to_f32(q.y & 0xffffu); v[3] = bf16_to_f32(q.y >> 16);
   }
@@ -57,12 +63,12 @@ __device__ __forceinline__ void load4a(const ST* p, float v[4]) {
 template <typename ST>
 __device__ __forceinline__ void store4a(ST* p, const float v[4]) {
   if constexpr (sizeof(ST) == 4) {
-    *reinterpret_cast<float4*>(p) = make_float4(v[0], v[1], v[2], v[3]);
+    __builtin_nontemporal_store(nt_f32x4{v[0], v[1], v[2], v[3]}, reinterpret_cast<nt_f32x4*>(p));
   } else {
-    uint2 q;
+    nt_u32x2 q;
     q.x = f32x2_to_bf16x2(v[0], v[1]);
     q.y = f32x2_to_bf16x2(v[2], v[3]);
-    *reinterpret_cast<uint2*>(p) = q;
+    __builtin_nontemporal_store(q, reinterpret_cast<nt_u32x2*>(p));
   }
 }
 
