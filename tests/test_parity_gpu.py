@@ -191,6 +191,35 @@ def test_batch_partition_invariance_and_determinism(nsa):
             assert np.array_equal(a, b)
 
 
+def test_repeat_calls_bitwise_with_claimed_tiles(nsa):
+    # 40 matrices of 1024 x 1536: 400 Gram tiles (4 diagonal per matrix) over
+    # at most 256 workgroups, so tiles are claimed from the per-XCD counters;
+    # repeated calls, and a split into other batches in between, must give
+    # the same bits (every tile computed once, counters zeroed per launch).
+    import torch
+    shapes = [(1024, 1536)] * 24 + [(1536, 1024)] * 16
+    case = workloads.random_case(17, shapes, "bf16")
+    outs = []
+    for cap in (0, 7 * 1024 * 1536, 0):
+        P, G, M = upload_case(case, "bf16")
+        nsa.muon_step(list(zip(P, G, M)), 0.02, 0.95, 5, batch_cap_elems=cap)
+        torch.cuda.synchronize()
+        outs.append(_bits(P))
+    for o in outs[1:]:
+        for a, b in zip(outs[0], o):
+            assert np.array_equal(a, b)
+    # and the result is the Muon update: spot-check two matrices against
+    # the oracle
+    sub = [case[0], case[30]]
+    ref = oracle_case(sub, 0.02, 0.95, 5)
+    P, G, M = upload_case(case, "bf16")
+    nsa.muon_step(list(zip(P, G, M)), 0.02, 0.95, 5)
+    torch.cuda.synchronize()
+    for c, i, (rp, _, _) in zip(sub, (0, 30), ref):
+        e = check_update(c["params"].as_f64(), from_device(P[i]), rp, "bf16", BF16_TOL)
+        assert e <= BF16_TOL, (i, e)
+
+
 def test_mixed_call_equals_per_group_calls(nsa):
     import torch
     shapes = [(256, 640), (128, 128), (640, 256), (128, 128), (200, 100)]
