@@ -28,7 +28,8 @@
  * Conventions shared by every entry point
  *   - Device memory: every matrix pointer (params, grads, momentum, in, out)
  *     is a DEVICE pointer to a contiguous row-major rows x cols matrix on
- *     the current HIP device, 16-byte aligned. The arrays that hold those
+ *     the current HIP device, 16-byte aligned (muon_step_views also takes
+ *     strided row-major views). The arrays that hold those
  *     pointers (and muon_matrix arrays, coefficient tables) are HOST memory;
  *     the library copies what it needs before returning, so the caller may
  *     free them immediately.
@@ -114,6 +115,13 @@ typedef struct muon_options {
                              so when some are, a fitted split can leave a
                              nearly empty last round: fit only groups that are
                              known to have none.                              */
+  int ns_dtype;           /* element type the NS iteration runs in. -1
+                             (default): `dtype`. MUON_BF16 with dtype MUON_F32:
+                             fp32 master params, grads and momentum, iterated
+                             on bf16 MFMA (section 6.6: bf16 NS; section 7.4:
+                             FP32 optimizer state); the update is applied to
+                             the fp32 params. MUON_F32 with dtype MUON_BF16:
+                             bf16 tensors iterated in fp32.                   */
 } muon_options;
 
 /* Fills *opts with the defaults above. */
@@ -145,11 +153,40 @@ int muon_group_step(void* const* params, const void* const* grads, float* const*
 int muon_step(const muon_matrix* mats, int num, float lr, float beta, int ns_steps,
               muon_dtype dtype, const muon_options* opts, void* stream);
 
+/* One logical matrix of a physical parameter, as a zero-copy strided view
+ * (section 6.6: the model adapter defines the matrices Muon sees inside a
+ * parameter -- heads of a fused QKV projection, gate and up halves of an
+ * FC1 weight, factors of an MLA projection -- and writes their updates back
+ * in place). Element (i, j) of the view is base[i*ld + j] for param, grad
+ * and momentum alike (the three share the parameter's layout).
+ *   ld: row stride in elements, 0 means cols (contiguous); otherwise
+ *       cols <= ld <= 2^31 - 1.
+ * Row blocks of a contiguous parameter (QKV heads, stacked gate/up) are
+ * views with ld = the parameter's cols; column blocks and interleaved rows
+ * use a larger ld. Views may share a parameter as long as no element
+ * belongs to two of them: views with equal ld are checked element-exactly,
+ * views with different ld must not share any byte range. Base pointers
+ * must be 16-byte aligned. */
+typedef struct muon_matrix_view {
+  void* param;        /* device, rows x cols view, dtype, updated in place  */
+  const void* grad;   /* device, rows x cols view, dtype, read only         */
+  float* momentum;    /* device, rows x cols view, float32, updated in place */
+  int rows, cols;
+  long long ld;       /* row stride in elements (0 = cols)                 */
+} muon_matrix_view;
+
+/* muon_step over strided logical-matrix views: each view is one matrix of
+ * its shape group, exactly as if it were a contiguous muon_matrix (the same
+ * arithmetic, bitwise). Errors as muon_step, plus ld < cols, ld > 2^31 - 1
+ * and views that share an element. */
+int muon_step_views(const muon_matrix_view* views, int num, float lr, float beta, int ns_steps,
+                    muon_dtype dtype, const muon_options* opts, void* stream);
+
 /* Orthogonalization only: out[i] = NS(in[i]) in in[i]'s orientation
  * (Frobenius normalisation then ns_steps iterations; no momentum, no
  * scale). in[i] and out[i] are device rows x cols matrices of `dtype`;
- * out may equal in. opts may be NULL (only eps, coeffs, batch_cap_elems
- * are used). */
+ * out may equal in. opts may be NULL (only eps, coeffs, batch_cap_elems,
+ * compute_units and ns_dtype are used). */
 int muon_orthogonalize(const void* const* in, void* const* out, int count, int m, int n,
                        int ns_steps, muon_dtype dtype, const muon_options* opts, void* stream);
 

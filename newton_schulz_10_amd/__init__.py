@@ -19,7 +19,7 @@ from typing import Iterable, List, Optional, Sequence, Tuple
 
 import torch  # loaded first: libmuon then binds to torch's HIP runtime
 
-__all__ = ["MuonError", "muon_group_step", "muon_step", "muon_orthogonalize", "plan_query",
+__all__ = ["MuonError", "muon_group_step", "muon_step", "muon_step_views", "muon_orthogonalize", "plan_query",
            "profile_enable", "profile_read", "version", "library_path", "load"]
 
 MUON_F32, MUON_BF16 = 0, 1
@@ -39,12 +39,17 @@ class Options(ctypes.Structure):
                 ("weight_decay", ctypes.c_float), ("scale_rule", ctypes.c_int),
                 ("rms_target", ctypes.c_float), ("eps", ctypes.c_float),
                 ("coeffs", ctypes.POINTER(ctypes.c_float)), ("batch_cap_elems", ctypes.c_size_t),
-                ("compute_units", ctypes.c_int)]
+                ("compute_units", ctypes.c_int), ("ns_dtype", ctypes.c_int)]
 
 
 class Matrix(ctypes.Structure):
     _fields_ = [("param", ctypes.c_void_p), ("grad", ctypes.c_void_p), ("momentum", ctypes.c_void_p),
                 ("rows", ctypes.c_int), ("cols", ctypes.c_int)]
+
+
+class MatrixView(ctypes.Structure):
+    _fields_ = [("param", ctypes.c_void_p), ("grad", ctypes.c_void_p), ("momentum", ctypes.c_void_p),
+                ("rows", ctypes.c_int), ("cols", ctypes.c_int), ("ld", ctypes.c_longlong)]
 
 
 class PlanBatch(ctypes.Structure):
@@ -59,7 +64,7 @@ class ProfileEntry(ctypes.Structure):
 
 
 _LIB = None
-SYMBOLS = ("muon_default_options", "muon_group_step", "muon_step", "muon_orthogonalize",
+SYMBOLS = ("muon_default_options", "muon_group_step", "muon_step", "muon_step_views", "muon_orthogonalize",
            "muon_plan_query", "muon_status_string", "muon_last_error", "muon_version",
            "muon_profile_enable", "muon_profile_read")
 
@@ -85,6 +90,8 @@ def load() -> ctypes.CDLL:
     L.muon_group_step.restype = i
     L.muon_step.argtypes = [ctypes.POINTER(Matrix), i, f, f, i, i, ctypes.POINTER(Options), vp]
     L.muon_step.restype = i
+    L.muon_step_views.argtypes = [ctypes.POINTER(MatrixView), i, f, f, i, i, ctypes.POINTER(Options), vp]
+    L.muon_step_views.restype = i
     L.muon_orthogonalize.argtypes = [ctypes.POINTER(vp), ctypes.POINTER(vp), i, i, i, i, i,
                                      ctypes.POINTER(Options), vp]
     L.muon_orthogonalize.restype = i
@@ -134,8 +141,11 @@ def _matrices(t: torch.Tensor, what: str) -> List[Tuple[int, int, int]]:
     raise ValueError(f"{what}: expected a 2-D matrix or a 3-D [E, M, N] bank, got {tuple(t.shape)}")
 
 
+_NS_DTYPES = {None: -1, torch.float32: MUON_F32, torch.bfloat16: MUON_BF16}
+
+
 def _options(nesterov=True, momentum_form="ema", weight_decay=0.0, scale_rule="rms", rms_target=0.2,
-             eps=1e-7, coeffs=None, batch_cap_elems=0, compute_units=0, ns_steps=5):
+             eps=1e-7, coeffs=None, batch_cap_elems=0, compute_units=0, ns_steps=5, ns_dtype=None):
     o = Options()
     load().muon_default_options(ctypes.byref(o))
     o.nesterov = 1 if nesterov else 0
@@ -153,6 +163,9 @@ def _options(nesterov=True, momentum_form="ema", weight_decay=0.0, scale_rule="r
         o.coeffs = ctypes.cast(keep, ctypes.POINTER(ctypes.c_float))
     o.batch_cap_elems = batch_cap_elems
     o.compute_units = compute_units
+    if ns_dtype not in _NS_DTYPES:
+        raise TypeError(f"ns_dtype must be None, torch.float32 or torch.bfloat16, got {ns_dtype}")
+    o.ns_dtype = _NS_DTYPES[ns_dtype]
     return o, keep
 
 
@@ -190,7 +203,9 @@ def muon_step(mats: Iterable[Tuple[torch.Tensor, torch.Tensor, torch.Tensor]], l
               beta: float = 0.95, ns_steps: int = 5, stream=None, **options) -> None:
     """C `muon_step`: one Muon step over (param, grad, momentum) triples of
     any shapes; options as in muon_options (nesterov, momentum_form,
-    weight_decay, scale_rule, rms_target, eps, coeffs, batch_cap_elems, compute_units)."""
+    weight_decay, scale_rule, rms_target, eps, coeffs, batch_cap_elems,
+    compute_units, ns_dtype: None for the tensors' dtype, or
+    torch.bfloat16 to iterate float32 master tensors on bf16 MFMA)."""
     rows = []
     dt = None
     for (p, g, m) in mats:
@@ -214,9 +229,45 @@ def muon_step(mats: Iterable[Tuple[torch.Tensor, torch.Tensor, torch.Tensor]], l
     del keep
 
 
+def muon_step_views(views: Iterable[Tuple[torch.Tensor, torch.Tensor, torch.Tensor]], lr: float,
+                    beta: float = 0.95, ns_steps: int = 5, stream=None, **options) -> None:
+    """C `muon_step_views`: one Muon step over logical matrices given as
+    strided 2-D views (param, grad, momentum) into physical parameters, e.g.
+    `W[h*d:(h+1)*d]` (a head of a fused QKV weight), `W[:, :k]` (a column
+    block) or `W[0::2]` (interleaved rows). Each view needs unit column
+    stride, and the three views of a matrix share one row stride. Updates
+    land in place in the viewed tensors. Options as in muon_step."""
+    rows = []
+    dt = None
+    for (p, g, m) in views:
+        for t, what in ((p, "param"), (g, "grad"), (m, "momentum")):
+            if not isinstance(t, torch.Tensor) or t.dim() != 2:
+                raise ValueError(f"{what}: expected a 2-D tensor view")
+            if t.stride(1) != 1 and t.shape[1] > 1:
+                raise ValueError(f"{what}: column stride must be 1, got {t.stride()}")
+        ld = p.stride(0) if p.shape[0] > 1 else p.shape[1]
+        for t, what in ((g, "grad"), (m, "momentum")):
+            if tuple(t.shape) != tuple(p.shape):
+                raise ValueError(f"{what}: shape {tuple(t.shape)} differs from param {tuple(p.shape)}")
+            if t.shape[0] > 1 and t.stride(0) != ld:
+                raise ValueError(f"{what}: row stride {t.stride(0)} differs from param's {ld}")
+        d = _dtype(p)
+        if dt is None:
+            dt = d
+        elif d != dt:
+            raise TypeError("all params of one call must share a dtype")
+        rows.append(MatrixView(p.data_ptr(), g.data_ptr(), m.data_ptr(), p.shape[0], p.shape[1], ld))
+    if not rows:
+        return
+    o, keep = _options(ns_steps=ns_steps, **options)
+    arr = (MatrixView * len(rows))(*rows)
+    _check(load().muon_step_views(arr, len(rows), lr, beta, ns_steps, dt, ctypes.byref(o), _stream(stream)))
+    del keep
+
+
 def muon_orthogonalize(inputs: Sequence[torch.Tensor], outputs: Sequence[torch.Tensor], ns_steps: int = 5,
                        stream=None, eps: float = 1e-7, coeffs=None, batch_cap_elems: int = 0,
-                       compute_units: int = 0) -> None:
+                       compute_units: int = 0, ns_dtype=None) -> None:
     """C `muon_orthogonalize`: outputs[i] = NS(inputs[i]) (same shapes)."""
     I = [x for t in inputs for x in _matrices(t, "inputs")]
     O = [x for t in outputs for x in _matrices(t, "outputs")]
@@ -229,7 +280,7 @@ def muon_orthogonalize(inputs: Sequence[torch.Tensor], outputs: Sequence[torch.T
         raise ValueError("all matrices must share one shape")
     dt = _dtype(inputs[0])
     o, keep = _options(eps=eps, coeffs=coeffs, batch_cap_elems=batch_cap_elems, compute_units=compute_units,
-                       ns_steps=ns_steps)
+                       ns_steps=ns_steps, ns_dtype=ns_dtype)
     arr = ctypes.c_void_p * len(I)
     _check(load().muon_orthogonalize(arr(*[p for p, _, _ in I]), arr(*[p for p, _, _ in O]), len(I), m, n,
                                      ns_steps, dt, ctypes.byref(o), _stream(stream)))
@@ -237,13 +288,13 @@ def muon_orthogonalize(inputs: Sequence[torch.Tensor], outputs: Sequence[torch.T
 
 
 def plan_query(shapes: Sequence[Tuple[int, int]], dtype: torch.dtype = torch.bfloat16,
-               batch_cap_elems: int = 0, compute_units: int = 0) -> dict:
+               batch_cap_elems: int = 0, compute_units: int = 0, ns_dtype=None) -> dict:
     """C `muon_plan_query` (host only): the batches and order muon_step would use."""
     L = load()
     n = len(shapes)
     rows = (ctypes.c_int * max(n, 1))(*[r for r, _ in shapes])
     cols = (ctypes.c_int * max(n, 1))(*[c for _, c in shapes])
-    o, _ = _options(batch_cap_elems=batch_cap_elems, compute_units=compute_units)
+    o, _ = _options(batch_cap_elems=batch_cap_elems, compute_units=compute_units, ns_dtype=ns_dtype)
     nb = ctypes.c_int(0)
     ws = ctypes.c_size_t(0)
     _check(L.muon_plan_query(rows, cols, n, _DTYPES[dtype], ctypes.byref(o), None, 0, ctypes.byref(nb), None,

@@ -24,6 +24,10 @@ namespace {
 
 constexpr int T = kEwTile;  // 64
 
+// The matrix table travels in the kernel argument block; keep it (with the
+// largest per-launch arguments) within 4 KiB.
+static_assert(sizeof(EwMats) + sizeof(MomentumArgs) <= 4096, "elementwise kernel arguments exceed 4 KiB");
+
 template <typename ST>
 __device__ __forceinline__ void load4(const ST* p, int valid, float v[4]) {
   // valid: number of in-range elements starting at p (0..4)
@@ -113,26 +117,27 @@ __global__ __launch_bounds__(256) void momentum_kernel(EwMats mats, MomentumArgs
   XT* x0 = static_cast<XT*>(a.x0) + (size_t)(a.first + mi) * a.mat_x;
   float ss = 0.0f;
   int nz = 0;   // any u of the tile not exactly 0 (NaN != 0 counts)
-  if (a.ptab && blockIdx.x == 0 && threadIdx.x == 0) a.ptab[a.first + mi] = ApplyEntry{mats.dst[mi], mats.tr[mi], 0};
+  const size_t ld = (size_t)mats.ld[mi];   // row stride of g and buf as stored
+  if (a.ptab && blockIdx.x == 0 && threadIdx.x == 0)
+    a.ptab[a.first + mi] = ApplyEntry{mats.dst[mi], mats.tr[mi], mats.ld[mi]};
 
-  // Interior tiles (all 64 x 64 elements in range, rows a multiple of 4
-  // long, so every 4-element access is whole and aligned) issue all their
+  // Interior tiles (all 64 x 64 elements in range, row stride a multiple
+  // of 4, so every 4-element access is whole and aligned) issue all their
   // loads before any arithmetic or store: four passes of loads in flight
   // per thread instead of one. Edge tiles take the general path below.
-  const int orig_cols = mats.tr[mi] ? a.m : a.n;   // row length of the original
-  const bool interior = (orig_cols % 4 == 0) && (ti + 1) * T <= a.m && (tj + 1) * T <= a.n;
+  const bool interior = (ld % 4 == 0) && (ti + 1) * T <= a.m && (tj + 1) * T <= a.n;
   if (interior && !mats.tr[mi]) {
     float gv[4][4], bv[4][4];
 #pragma unroll
     for (int p = 0; p < 4; ++p) {
-      const size_t off = (size_t)(ti * T + ty + 16 * p) * a.n + tj * T + tx * 4;
+      const size_t off = (size_t)(ti * T + ty + 16 * p) * ld + tj * T + tx * 4;
       load4a<GT>(g + off, gv[p]);
       if (a.has_buf) load4a<float>(buf + off, bv[p]);
     }
 #pragma unroll
     for (int p = 0; p < 4; ++p) {
       const int i = ti * T + ty + 16 * p;
-      const size_t off = (size_t)i * a.n + tj * T + tx * 4;
+      const size_t off = (size_t)i * ld + tj * T + tx * 4;
       float u[4];
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
@@ -147,13 +152,13 @@ __global__ __launch_bounds__(256) void momentum_kernel(EwMats mats, MomentumArgs
     float gv[4][4], bv[4][4];
 #pragma unroll
     for (int p = 0; p < 4; ++p) {
-      const size_t off = (size_t)(tj * T + ty + 16 * p) * a.m + ti * T + tx * 4;
+      const size_t off = (size_t)(tj * T + ty + 16 * p) * ld + ti * T + tx * 4;
       load4a<GT>(g + off, gv[p]);
       if (a.has_buf) load4a<float>(buf + off, bv[p]);
     }
 #pragma unroll
     for (int p = 0; p < 4; ++p) {
-      const size_t off = (size_t)(tj * T + ty + 16 * p) * a.m + ti * T + tx * 4;
+      const size_t off = (size_t)(tj * T + ty + 16 * p) * ld + ti * T + tx * 4;
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         const float u = momentum_elem(gv[p][e], bv[p][e], a);
@@ -182,8 +187,8 @@ __global__ __launch_bounds__(256) void momentum_kernel(EwMats mats, MomentumArgs
       if (i < a.m) {
         const int valid = clamp4(a.n - j);
         float gv[4], bv[4] = {0.f, 0.f, 0.f, 0.f};
-        load4<GT>(g + (size_t)i * a.n + j, valid, gv);
-        if (a.has_buf) load4<float>(buf + (size_t)i * a.n + j, valid, bv);
+        load4<GT>(g + (size_t)i * ld + j, valid, gv);
+        if (a.has_buf) load4<float>(buf + (size_t)i * ld + j, valid, bv);
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           if (e < valid) {
@@ -192,7 +197,7 @@ __global__ __launch_bounds__(256) void momentum_kernel(EwMats mats, MomentumArgs
             nz |= u[e] != 0.0f;
           }
         }
-        if (a.has_buf) store4<float>(buf + (size_t)i * a.n + j, valid, bv);
+        if (a.has_buf) store4<float>(buf + (size_t)i * ld + j, valid, bv);
       }
       store4<XT>(x0 + (size_t)i * a.n_pad + j, 4, u);
     }
@@ -208,8 +213,8 @@ __global__ __launch_bounds__(256) void momentum_kernel(EwMats mats, MomentumArgs
       if (r < a.n) {
         const int valid = clamp4(a.m - c);
         float gv[4], bv[4] = {0.f, 0.f, 0.f, 0.f};
-        load4<GT>(g + (size_t)r * a.m + c, valid, gv);
-        if (a.has_buf) load4<float>(buf + (size_t)r * a.m + c, valid, bv);
+        load4<GT>(g + (size_t)r * ld + c, valid, gv);
+        if (a.has_buf) load4<float>(buf + (size_t)r * ld + c, valid, bv);
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           if (e < valid) {
@@ -218,7 +223,7 @@ __global__ __launch_bounds__(256) void momentum_kernel(EwMats mats, MomentumArgs
             nz |= u[e] != 0.0f;
           }
         }
-        if (a.has_buf) store4<float>(buf + (size_t)r * a.m + c, valid, bv);
+        if (a.has_buf) store4<float>(buf + (size_t)r * ld + c, valid, bv);
       }
 #pragma unroll
       for (int e = 0; e < 4; ++e) tile[ty + 16 * p][tx * 4 + e] = u[e];
@@ -276,9 +281,10 @@ __global__ __launch_bounds__(256) void apply_kernel(EwMats mats, ApplyArgs a) {
   if (a.dead_only && !zo) return;
   PT* dst = static_cast<PT*>(mats.dst[mi]);
   const PT* src = static_cast<const PT*>(mats.src[mi]);
+  const size_t ld = (size_t)mats.ld[mi];   // row stride of src and dst as stored
 
   // Interior tiles: all loads first (see momentum_kernel).
-  const bool interior = ((tr ? a.m : a.n) % 4 == 0) && (ti + 1) * T <= a.m && (tj + 1) * T <= a.n;
+  const bool interior = (ld % 4 == 0) && (ti + 1) * T <= a.m && (tj + 1) * T <= a.n;
   if (interior && !tr) {
     float o[4][4], pv[4][4];
 #pragma unroll
@@ -286,7 +292,7 @@ __global__ __launch_bounds__(256) void apply_kernel(EwMats mats, ApplyArgs a) {
       const int i = ti * T + ty + 16 * p, j = tj * T + tx * 4;
       load4a<XT>(x + (size_t)i * a.n_pad + j, o[p]);
       if (zo) o[p][0] = o[p][1] = o[p][2] = o[p][3] = 0.0f;
-      if (a.mode == 0) load4a<PT>(src + (size_t)i * a.n + j, pv[p]);
+      if (a.mode == 0) load4a<PT>(src + (size_t)i * ld + j, pv[p]);
     }
 #pragma unroll
     for (int p = 0; p < 4; ++p) {
@@ -296,7 +302,7 @@ __global__ __launch_bounds__(256) void apply_kernel(EwMats mats, ApplyArgs a) {
         const float oe = o[p][e] * os;
         pv[p][e] = a.mode == 0 ? fmaf(-gamma, oe, a.alpha * pv[p][e]) : oe;
       }
-      store4a<PT>(dst + (size_t)i * a.n + j, pv[p]);
+      store4a<PT>(dst + (size_t)i * ld + j, pv[p]);
     }
     return;
   }
@@ -306,7 +312,7 @@ __global__ __launch_bounds__(256) void apply_kernel(EwMats mats, ApplyArgs a) {
     for (int p = 0; p < 4; ++p) {
       load4a<XT>(x + (size_t)(ti * T + ty + 16 * p) * a.n_pad + tj * T + tx * 4, o[p]);
       if (zo) o[p][0] = o[p][1] = o[p][2] = o[p][3] = 0.0f;
-      if (a.mode == 0) load4a<PT>(src + (size_t)(tj * T + ty + 16 * p) * a.m + ti * T + tx * 4, pv[p]);
+      if (a.mode == 0) load4a<PT>(src + (size_t)(tj * T + ty + 16 * p) * ld + ti * T + tx * 4, pv[p]);
     }
 #pragma unroll
     for (int p = 0; p < 4; ++p)
@@ -321,7 +327,7 @@ __global__ __launch_bounds__(256) void apply_kernel(EwMats mats, ApplyArgs a) {
         const float oe = tile[tx * 4 + e][ty + 16 * p] * os;
         pv[p][e] = a.mode == 0 ? fmaf(-gamma, oe, a.alpha * pv[p][e]) : oe;
       }
-      store4a<PT>(dst + (size_t)r * a.m + c, pv[p]);
+      store4a<PT>(dst + (size_t)r * ld + c, pv[p]);
     }
     return;
   }
@@ -337,13 +343,13 @@ __global__ __launch_bounds__(256) void apply_kernel(EwMats mats, ApplyArgs a) {
       float o[4], pv[4] = {0.f, 0.f, 0.f, 0.f};
       load4<XT>(x + (size_t)i * a.n_pad + j, 4, o);
       if (zo) o[0] = o[1] = o[2] = o[3] = 0.0f;
-      if (a.mode == 0) load4<PT>(src + (size_t)i * a.n + j, valid, pv);
+      if (a.mode == 0) load4<PT>(src + (size_t)i * ld + j, valid, pv);
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         const float oe = o[e] * os;
         pv[e] = a.mode == 0 ? fmaf(-gamma, oe, a.alpha * pv[e]) : oe;
       }
-      store4<PT>(dst + (size_t)i * a.n + j, valid, pv);
+      store4<PT>(dst + (size_t)i * ld + j, valid, pv);
     }
   } else {
     // Original is n x m; element (r, c) takes O[c][r].
@@ -365,13 +371,13 @@ __global__ __launch_bounds__(256) void apply_kernel(EwMats mats, ApplyArgs a) {
       const int valid = clamp4(a.m - c);
       if (valid == 0) continue;
       float pv[4] = {0.f, 0.f, 0.f, 0.f};
-      if (a.mode == 0) load4<PT>(src + (size_t)r * a.m + c, valid, pv);
+      if (a.mode == 0) load4<PT>(src + (size_t)r * ld + c, valid, pv);
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         const float oe = tile[tx * 4 + e][ty + 16 * p] * os;
         pv[e] = a.mode == 0 ? fmaf(-gamma, oe, a.alpha * pv[e]) : oe;
       }
-      store4<PT>(dst + (size_t)r * a.m + c, valid, pv);
+      store4<PT>(dst + (size_t)r * ld + c, valid, pv);
     }
   }
 }

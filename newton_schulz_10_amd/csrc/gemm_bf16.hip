@@ -558,6 +558,7 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& g, int mat, int I, int
       // Reads of a batch (T, then p) are issued before its stores.
       const ApplyEntry ent = g.ptab[mat];
       bf16_t* const dst = static_cast<bf16_t*>(ent.dst);
+      const size_t ld = (size_t)ent.ld;   // row stride of p as stored
       const float gam = g.gamma[ent.tr], alpha = g.alpha;
       const bool upd = g.apply_mode == 0;
       auto apply8 = [&](uint4 o, uint4 pv) {
@@ -573,7 +574,7 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& g, int mat, int I, int
         return uint4{r[0], r[1], r[2], r[3]};
       };
       if (!ent.tr) {
-        // Wide member: tile rows are rows of p (row length n).
+        // Wide member: tile rows are rows of p (n elements, ld apart).
 #pragma unroll 1
         for (int r0 = 0; r0 < (PR * TC8) / kThreads; r0 += kBatch) {
           uint4 v[kBatch], pv[kBatch];
@@ -586,7 +587,7 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& g, int mat, int I, int
             v[u] = *reinterpret_cast<const uint4*>(T + i * QR + ((c ^ eswz(i)) << 3));
             const int gi = I * TILE + i, gj = q0 + 8 * c;
             ok[u] = gi < g.m && gj < g.n;
-            off[u] = ok[u] ? (size_t)gi * g.n + gj : 0;
+            off[u] = ok[u] ? gi * ld + gj : 0;
             pv[u] = upd ? *reinterpret_cast<const uint4*>(dst + off[u]) : uint4{0u, 0u, 0u, 0u};
           }
           keep_batch(v);
@@ -611,7 +612,7 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& g, int mat, int I, int
             v[u] = tr8(i0, jb);
             const int gj = q0 + jb + jj, gi = I * TILE + i0 + 8 * grp;
             ok[u] = gj < g.n && gi < g.m;
-            off[u] = ok[u] ? (size_t)gj * g.m + gi : 0;
+            off[u] = ok[u] ? gj * ld + gi : 0;
             pv[u] = upd ? *reinterpret_cast<const uint4*>(dst + off[u]) : uint4{0u, 0u, 0u, 0u};
           }
           keep_batch(v);

@@ -18,6 +18,7 @@ struct EwMats {
   const void* src[kEwChunk];  // momentum pass: grad (or NS input); apply: param
   float* buf[kEwChunk];       // momentum pass: momentum buffer (may be unused)
   void* dst[kEwChunk];        // apply: param or output matrix
+  int ld[kEwChunk];            // row stride (elements) of src, buf and dst as stored
   unsigned char tr[kEwChunk]; // 1 when the matrix is stored tall (rows > cols)
 };
 
@@ -27,7 +28,7 @@ struct EwMats {
 struct ApplyEntry {
   void* dst;   // param, updated in place (step), or the output (orthogonalize)
   int tr;      // 1 when the matrix is stored tall (rows > cols)
-  int pad;
+  int ld;      // row stride of dst (elements), a multiple of 8
 };
 
 // Momentum pass: reads each matrix's source (and momentum buffer), writes

@@ -118,7 +118,13 @@ struct MatRef {
   const void* src;    // grad (step) or input (orthogonalize)
   float* mom;         // momentum (step) or nullptr
   int rows, cols;
+  int ld;             // row stride in elements of param, src and mom (>= cols)
 };
+
+// Element type the NS iteration runs in: options.ns_dtype, or the tensors'.
+muon_dtype ns_type(const muon_options& o, muon_dtype dtype) {
+  return o.ns_dtype < 0 ? dtype : static_cast<muon_dtype>(o.ns_dtype);
+}
 
 double update_scale(const muon_options& o, int rows, int cols) {
   switch (o.scale_rule) {
@@ -147,9 +153,12 @@ int run(const std::vector<MatRef>& mats, float lr, float beta, int ns_steps, muo
   const int num = (int)mats.size();
   std::vector<int> rows(num), cols(num);
   for (int i = 0; i < num; ++i) { rows[i] = mats[i].rows; cols[i] = mats[i].cols; }
+  // Tensors (params, grads, in/out) are `dtype`; the NS iterate and its
+  // workspace are `ns`, which also sets the plan's padding and layout.
+  const muon_dtype ns = ns_type(o, dtype);
   Plan plan;
   std::string err;
-  int rc = build_plan(rows.data(), cols.data(), num, dtype, o.batch_cap_elems, fit_units(o), plan, err);
+  int rc = build_plan(rows.data(), cols.data(), num, ns, o.batch_cap_elems, fit_units(o), plan, err);
   if (rc) return fail(rc, err);
 
   if (const char* f = std::getenv("MUON_TEST_FAIL_ALLOC"))
@@ -169,14 +178,15 @@ int run(const std::vector<MatRef>& mats, float lr, float beta, int ns_steps, muo
                 std::to_string(plan.workspace_bytes) + " bytes failed: " + hipGetErrorString(e));
   }
 
-  const bool bf16 = dtype == MUON_BF16;
-  const size_t es = dtype_size(dtype);
+  const bool bf16 = ns == MUON_BF16;           // NS kernels: bf16 MFMA, else fp32
+  const bool t_bf16 = dtype == MUON_BF16;      // params / grads / in / out
+  const size_t es = dtype_size(dtype), wes = dtype_size(ns);
   char* W = static_cast<char*>(ws);
   const float kg = o.momentum_form == 0 ? 1.0f - beta : 1.0f;
   int status = MUON_OK;
 
   for (const Batch& B : plan.batches) {
-    const Layout L = batch_layout(B.count, B.m_pad, B.n_pad, dtype);
+    const Layout L = batch_layout(B.count, B.m_pad, B.n_pad, ns);
     void* x0 = W + L.x0;
     void* x1 = W + L.x1;
     void* Am = W + L.a;
@@ -193,9 +203,11 @@ int run(const std::vector<MatRef>& mats, float lr, float beta, int ns_steps, muo
     float* scales = reinterpret_cast<float*>(W + L.scales);
     ApplyEntry* ptab = reinterpret_cast<ApplyEntry*>(W + L.ptab);
     const double elems = (double)B.m * B.n;
-    // bf16 with at least one NS step: the apply runs inside the last Update
-    // GEMM (it needs whole 16 B runs along rows of both orientations).
-    const bool fused_apply = bf16 && ns_steps > 0 && B.m % 8 == 0 && B.n % 8 == 0;
+    // bf16 tensors and NS with at least one NS step: the apply runs inside
+    // the last Update GEMM (it needs whole, aligned 16 B runs along rows of
+    // both orientations, so every row stride is a multiple of 8).
+    bool fused_apply = bf16 && t_bf16 && ns_steps > 0 && B.m % 8 == 0 && B.n % 8 == 0;
+    for (int k = 0; k < B.count && fused_apply; ++k) fused_apply = mats[plan.order[B.first + k]].ld % 8 == 0;
     const float apply_alpha = (float)(1.0 - (double)lr * (double)o.weight_decay);
     const float apply_gamma[2] = {(float)((double)lr * update_scale(o, B.m, B.n)),
                                   (float)((double)lr * update_scale(o, B.n, B.m))};
@@ -210,6 +222,7 @@ int run(const std::vector<MatRef>& mats, float lr, float beta, int ns_steps, muo
         em.src[k] = r.src;
         em.buf[k] = r.mom;
         em.dst[k] = r.param;
+        em.ld[k] = r.ld;
         em.tr[k] = r.rows > r.cols ? 1 : 0;
       }
       MomentumArgs a;
@@ -218,9 +231,9 @@ int run(const std::vector<MatRef>& mats, float lr, float beta, int ns_steps, muo
       a.partials = partials; a.nonzero = nonzero; a.has_buf = orthogonalize_only ? 0 : 1;
       a.beta = beta; a.kg = kg; a.nesterov = o.nesterov;
       a.ptab = fused_apply ? ptab : nullptr;
-      const double bytes = cn * elems * ((orthogonalize_only ? es : es + 4 + 4) + es);
+      const double bytes = cn * elems * ((orthogonalize_only ? es : es + 4 + 4) + wes);
       ProfScope ps("momentum", 0.0, bytes, stream);
-      e = launch_momentum(em, a, bf16, bf16, stream);
+      e = launch_momentum(em, a, t_bf16, bf16, stream);
       if (e != hipSuccess) status = hip_fail(e, "momentum kernel launch");
     }
     if (status) break;
@@ -298,6 +311,7 @@ int run(const std::vector<MatRef>& mats, float lr, float beta, int ns_steps, muo
         const MatRef& r = mats[plan.order[B.first + c0 + k]];
         em.src[k] = r.param;
         em.dst[k] = r.param;
+        em.ld[k] = r.ld;
         em.tr[k] = r.rows > r.cols ? 1 : 0;
       }
       ApplyArgs a;
@@ -309,9 +323,9 @@ int run(const std::vector<MatRef>& mats, float lr, float beta, int ns_steps, muo
       a.alpha = apply_alpha;
       a.gamma[0] = apply_gamma[0];
       a.gamma[1] = apply_gamma[1];
-      const double bytes = cn * elems * (orthogonalize_only ? es + es : es + es + es);
+      const double bytes = cn * elems * (orthogonalize_only ? wes + es : wes + es + es);
       ProfScope ps("apply", 0.0, bytes, stream);
-      e = launch_apply(em, a, bf16, bf16, stream);
+      e = launch_apply(em, a, t_bf16, bf16, stream);
       if (e != hipSuccess) status = hip_fail(e, "apply kernel launch");
     }
     if (status) break;
@@ -350,16 +364,16 @@ int validate_mats(const std::vector<MatRef>& mats, muon_dtype dtype, bool orthog
     if ((rc = check_ptr(r.param, pn, i, err))) return fail(rc, err);
     if ((rc = check_ptr(r.src, sn, i, err))) return fail(rc, err);
     if (!orthogonalize_only && (rc = check_ptr(r.mom, "momentum", i, err))) return fail(rc, err);
-    const unsigned long long elems = (unsigned long long)r.rows * (unsigned long long)r.cols;
-    const auto lo = [](const void* p) { return (unsigned long long)reinterpret_cast<uintptr_t>(p); };
+    const unsigned long long rows = (unsigned long long)r.rows, cols = (unsigned long long)r.cols,
+                             ld = (unsigned long long)r.ld;
     if (orthogonalize_only) {
       // out may be exactly in (in place); any other overlap is an error.
-      if (r.param != r.src) ranges.push_back({lo(r.src), lo(r.src) + elems * es, sn, i});
-      ranges.push_back({lo(r.param), lo(r.param) + elems * es, pn, i});
+      if (r.param != r.src) ranges.push_back(strided_range(r.src, rows, cols * es, ld * es, sn, i));
+      ranges.push_back(strided_range(r.param, rows, cols * es, ld * es, pn, i));
     } else {
-      ranges.push_back({lo(r.param), lo(r.param) + elems * es, pn, i});
-      ranges.push_back({lo(r.src), lo(r.src) + elems * es, sn, i});
-      ranges.push_back({lo(r.mom), lo(r.mom) + elems * 4, "momentum", i});
+      ranges.push_back(strided_range(r.param, rows, cols * es, ld * es, pn, i));
+      ranges.push_back(strided_range(r.src, rows, cols * es, ld * es, sn, i));
+      ranges.push_back(strided_range(r.mom, rows, cols * 4, ld * 4, "momentum", i));
     }
   }
   int rc = check_no_overlap(ranges, err);
@@ -389,7 +403,37 @@ int muon_step(const muon_matrix* mats, int num, float lr, float beta, int ns_ste
     if (rc) return rc;
     std::vector<MatRef> v(num);
     for (int i = 0; i < num; ++i)
-      v[i] = MatRef{mats[i].param, mats[i].grad, mats[i].momentum, mats[i].rows, mats[i].cols};
+      v[i] = MatRef{mats[i].param, mats[i].grad, mats[i].momentum, mats[i].rows, mats[i].cols, mats[i].cols};
+    rc = validate_mats(v, dtype, false);
+    if (rc) return rc;
+    return run(v, lr, beta, ns_steps, dtype, o, false, static_cast<hipStream_t>(stream));
+  } catch (const std::exception& ex) {
+    return fail(MUON_ERR_HIP, std::string("internal error: ") + ex.what());
+  } catch (...) {
+    return fail(MUON_ERR_HIP, "internal error");
+  }
+}
+
+int muon_step_views(const muon_matrix_view* views, int num, float lr, float beta, int ns_steps,
+                    muon_dtype dtype, const muon_options* opts, void* stream) {
+  try {
+    g_err.clear();
+    if (num < 0) return fail(MUON_ERR_INVALID_ARGUMENT, "num < 0");
+    if (num > 0 && !views) return fail(MUON_ERR_INVALID_ARGUMENT, "views is NULL");
+    muon_options o;
+    int rc = validate_common(lr, beta, ns_steps, dtype, opts, o);
+    if (rc) return rc;
+    std::vector<MatRef> v(num);
+    for (int i = 0; i < num; ++i) {
+      const muon_matrix_view& w = views[i];
+      std::string err;
+      if ((rc = check_shape(w.rows, w.cols, err, i))) return fail(rc, err);
+      const long long ld = w.ld == 0 ? (long long)w.cols : w.ld;
+      if (ld < w.cols || ld > 0x7fffffffLL)
+        return fail(MUON_ERR_INVALID_ARGUMENT, "views[" + std::to_string(i) + "].ld = " + std::to_string(w.ld) +
+                                                   " outside [cols, 2^31 - 1]");
+      v[i] = MatRef{w.param, w.grad, w.momentum, w.rows, w.cols, (int)ld};
+    }
     rc = validate_mats(v, dtype, false);
     if (rc) return rc;
     return run(v, lr, beta, ns_steps, dtype, o, false, static_cast<hipStream_t>(stream));
@@ -415,7 +459,7 @@ int muon_group_step(void* const* params, const void* const* grads, float* const*
       if ((rc = check_shape(m, n, err))) return fail(rc, err);
     }
     std::vector<MatRef> v(count);
-    for (int i = 0; i < count; ++i) v[i] = MatRef{params[i], grads[i], momentum[i], m, n};
+    for (int i = 0; i < count; ++i) v[i] = MatRef{params[i], grads[i], momentum[i], m, n, n};
     rc = validate_mats(v, dtype, false);
     if (rc) return rc;
     return run(v, lr, beta, ns_steps, dtype, o, false, static_cast<hipStream_t>(stream));
@@ -440,7 +484,7 @@ int muon_orthogonalize(const void* const* in, void* const* out, int count, int m
       if ((rc = check_shape(m, n, err))) return fail(rc, err);
     }
     std::vector<MatRef> v(count);
-    for (int i = 0; i < count; ++i) v[i] = MatRef{out[i], in[i], nullptr, m, n};
+    for (int i = 0; i < count; ++i) v[i] = MatRef{out[i], in[i], nullptr, m, n, n};
     rc = validate_mats(v, dtype, true);
     if (rc) return rc;
     return run(v, 0.0f, 0.0f, ns_steps, dtype, o, true, static_cast<hipStream_t>(stream));
@@ -461,7 +505,9 @@ int muon_plan_query(const int* rows, const int* cols, int num, muon_dtype dtype,
     Plan plan;
     std::string err;
     if (o.compute_units < -1) return fail(MUON_ERR_INVALID_ARGUMENT, "options.compute_units must be >= -1");
-    int rc = build_plan(rows, cols, num, dtype, o.batch_cap_elems, fit_units(o), plan, err);
+    if (o.ns_dtype != -1 && o.ns_dtype != MUON_F32 && o.ns_dtype != MUON_BF16)
+      return fail(MUON_ERR_INVALID_ARGUMENT, "options.ns_dtype must be -1, MUON_F32 or MUON_BF16");
+    int rc = build_plan(rows, cols, num, ns_type(o, dtype), o.batch_cap_elems, fit_units(o), plan, err);
     if (rc) return fail(rc, err);
     if (cap > 0 && !batches) return fail(MUON_ERR_INVALID_ARGUMENT, "batches is NULL with cap > 0");
     for (int i = 0; i < cap && i < (int)plan.batches.size(); ++i) {
@@ -491,7 +537,7 @@ const char* muon_status_string(int status) {
 
 const char* muon_last_error(void) { return g_err.c_str(); }
 
-int muon_version(void) { return 100; }
+int muon_version(void) { return 200; }
 
 int muon_profile_enable(int on) {
   std::lock_guard<std::mutex> lk(g_prof_mu);

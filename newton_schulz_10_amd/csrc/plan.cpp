@@ -151,6 +151,7 @@ void default_options(muon_options& o) {
   o.coeffs = nullptr;
   o.batch_cap_elems = MUON_DEFAULT_BATCH_CAP;
   o.compute_units = 0;
+  o.ns_dtype = -1;
 }
 
 int check_options(const muon_options& o, int ns_steps, std::string& err) {
@@ -161,6 +162,9 @@ int check_options(const muon_options& o, int ns_steps, std::string& err) {
   if (!std::isfinite(o.rms_target)) { err = "options.rms_target is not finite"; return MUON_ERR_INVALID_ARGUMENT; }
   if (!(o.eps >= 0.0f) || !std::isfinite(o.eps)) { err = "options.eps must be finite and >= 0"; return MUON_ERR_INVALID_ARGUMENT; }
   if (o.compute_units < -1) { err = "options.compute_units must be >= -1"; return MUON_ERR_INVALID_ARGUMENT; }
+  if (o.ns_dtype != -1 && o.ns_dtype != MUON_F32 && o.ns_dtype != MUON_BF16) {
+    err = "options.ns_dtype must be -1, MUON_F32 or MUON_BF16"; return MUON_ERR_INVALID_ARGUMENT;
+  }
   if (o.coeffs) {
     for (int i = 0; i < 3 * ns_steps; ++i)
       if (!std::isfinite(o.coeffs[i])) {
@@ -194,14 +198,46 @@ int check_ptr(const void* p, const char* what, int index, std::string& err) {
   return MUON_OK;
 }
 
+Range strided_range(const void* p, unsigned long long rows, unsigned long long row_bytes,
+                    unsigned long long ld_bytes, const char* what, int index) {
+  Range r;
+  r.lo = (unsigned long long)reinterpret_cast<uintptr_t>(p);
+  r.hi = r.lo + (rows > 0 ? (rows - 1) * ld_bytes + row_bytes : 0);
+  r.what = what;
+  r.index = index;
+  r.rows = rows;
+  r.row_bytes = row_bytes;
+  r.ld_bytes = ld_bytes;
+  return r;
+}
+
+namespace {
+
+// Whether two blocks with intersecting spans share a byte; a.lo <= b.lo.
+// With equal strides L, b's rows sit at offset d = q L + rr in a's frame:
+// b row k covers bytes [rr, rr + wb) of a's row q + k, wrapping into row
+// q + k + 1 when rr + wb > L.
+bool blocks_overlap(const Range& a, const Range& b) {
+  const unsigned long long L = a.ld_bytes;
+  if (L != b.ld_bytes || L == 0 || a.row_bytes > L || b.row_bytes > L) return true;
+  const unsigned long long d = b.lo - a.lo, q = d / L, rr = d % L;
+  if (rr < a.row_bytes && q < a.rows) return true;                 // b rows q.. on a's columns
+  if (rr + b.row_bytes > L && q + 1 < a.rows) return true;         // wrapped part, a's rows q+1..
+  return false;
+}
+
+}  // namespace
+
 int check_no_overlap(std::vector<Range>& r, std::string& err) {
   std::sort(r.begin(), r.end(), [](const Range& a, const Range& b) { return a.lo < b.lo; });
-  for (size_t i = 1; i < r.size(); ++i) {
-    if (r[i].lo < r[i - 1].hi) {
-      std::ostringstream s;
-      s << r[i - 1].what << "[" << r[i - 1].index << "] overlaps " << r[i].what << "[" << r[i].index << "]";
-      err = s.str();
-      return MUON_ERR_INVALID_ARGUMENT;
+  for (size_t i = 0; i < r.size(); ++i) {
+    for (size_t j = i + 1; j < r.size() && r[j].lo < r[i].hi; ++j) {
+      if (r[i].hi > r[i].lo && r[j].hi > r[j].lo && blocks_overlap(r[i], r[j])) {
+        std::ostringstream s;
+        s << r[i].what << "[" << r[i].index << "] overlaps " << r[j].what << "[" << r[j].index << "]";
+        err = s.str();
+        return MUON_ERR_INVALID_ARGUMENT;
+      }
     }
   }
   return MUON_OK;

@@ -77,10 +77,20 @@ int check_scalars(float lr, float beta, int ns_steps, muon_dtype dtype, std::str
 int check_shape(int m, int n, std::string& err, int index = -1);
 int check_ptr(const void* p, const char* what, int index, std::string& err);
 
-// Address ranges of the matrices must not overlap (params, grads, momentum
-// of all matrices). `ranges` is a list of [begin, end) byte ranges with a
-// label for the message.
-struct Range { unsigned long long lo, hi; const char* what; int index; };
+// The matrices (params, grads, momentum of all matrices) must not share
+// any byte. Each is a strided block: `rows` rows of `row_bytes` bytes,
+// `ld_bytes` apart, from `lo`; a contiguous matrix is the case ld_bytes ==
+// row_bytes. Blocks whose spans [lo, hi) intersect are compared exactly
+// when their strides are equal (interleaved views of one parameter) and
+// count as overlapping otherwise.
+struct Range {
+  unsigned long long lo, hi;   // span: hi = lo + (rows-1)*ld_bytes + row_bytes
+  const char* what;
+  int index;
+  unsigned long long rows, row_bytes, ld_bytes;
+};
+Range strided_range(const void* p, unsigned long long rows, unsigned long long row_bytes,
+                    unsigned long long ld_bytes, const char* what, int index);
 int check_no_overlap(std::vector<Range>& ranges, std::string& err);
 
 }  // namespace muon

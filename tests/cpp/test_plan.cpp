@@ -106,8 +106,54 @@ int main() {
     muon_options o;
     default_options(o);
     CHECK(check_options(o, 5, err) == MUON_OK);
+    CHECK(o.ns_dtype == -1);
     o.scale_rule = 3;
     CHECK(check_options(o, 5, err) == MUON_ERR_INVALID_ARGUMENT);
+    default_options(o);
+    o.ns_dtype = 2;
+    CHECK(check_options(o, 5, err) == MUON_ERR_INVALID_ARGUMENT);
+    o.ns_dtype = MUON_BF16;
+    CHECK(check_options(o, 5, err) == MUON_OK);
+  }
+  // Strided views of one parameter (bytes; a 4 x 64-byte parameter at 0x1000).
+  {
+    const auto at = [](unsigned long long a) { return reinterpret_cast<const void*>(uintptr_t(a)); };
+    // Interleaved rows (even / odd rows, stride 128): disjoint.
+    std::vector<Range> il = {strided_range(at(0x1000), 2, 64, 128, "params", 0),
+                             strided_range(at(0x1040), 2, 64, 128, "params", 1)};
+    CHECK(check_no_overlap(il, err) == MUON_OK);
+    // Column halves (32 bytes each of 64-byte rows): disjoint; a third view
+    // covering bytes 16..48 of every row meets both.
+    std::vector<Range> ch = {strided_range(at(0x1000), 4, 32, 64, "params", 0),
+                             strided_range(at(0x1020), 4, 32, 64, "params", 1)};
+    CHECK(check_no_overlap(ch, err) == MUON_OK);
+    ch.push_back(strided_range(at(0x1010), 4, 32, 64, "params", 2));
+    CHECK(check_no_overlap(ch, err) == MUON_ERR_INVALID_ARGUMENT);
+    // A view whose rows wrap into the next row of the other: row 0 of b
+    // covers bytes 48..80, i.e. byte 0..16 of a's row 1.
+    std::vector<Range> wr = {strided_range(at(0x1000), 2, 16, 64, "params", 0),
+                             strided_range(at(0x1030), 1, 32, 64, "grads", 0)};
+    CHECK(check_no_overlap(wr, err) == MUON_ERR_INVALID_ARGUMENT);
+    std::vector<Range> wr_ok = {strided_range(at(0x1000), 1, 16, 64, "params", 0),
+                                strided_range(at(0x1030), 1, 32, 64, "grads", 0)};
+    CHECK(check_no_overlap(wr_ok, err) == MUON_OK);
+    // Row blocks below one another: disjoint; one row more and they meet.
+    std::vector<Range> rb = {strided_range(at(0x1000), 2, 64, 64, "params", 0),
+                             strided_range(at(0x1080), 2, 64, 64, "params", 1)};
+    CHECK(check_no_overlap(rb, err) == MUON_OK);
+    rb[0] = strided_range(at(0x1000), 3, 64, 64, "params", 0);
+    CHECK(check_no_overlap(rb, err) == MUON_ERR_INVALID_ARGUMENT);
+    // Different strides with intersecting spans count as overlapping.
+    std::vector<Range> ds = {strided_range(at(0x1000), 2, 32, 128, "params", 0),
+                             strided_range(at(0x1040), 2, 32, 64, "params", 1)};
+    CHECK(check_no_overlap(ds, err) == MUON_ERR_INVALID_ARGUMENT);
+    // A long block that meets a block two places after it in address order.
+    std::vector<Range> far = {strided_range(at(0x1000), 4, 16, 64, "params", 0),
+                              strided_range(at(0x1010), 1, 16, 64, "params", 1),
+                              strided_range(at(0x1020), 1, 16, 64, "params", 2),
+                              strided_range(at(0x10c0), 1, 16, 64, "params", 3)};
+    CHECK(check_no_overlap(far, err) == MUON_ERR_INVALID_ARGUMENT);
+    CHECK(err == "params[0] overlaps params[3]");
   }
   std::printf(failures ? "planner tests: %d failures\n" : "planner tests: ok\n", failures);
   return failures ? 1 : 0;

@@ -197,3 +197,75 @@ def test_alloc_failure_injection_is_host_side(lib, monkeypatch):
     good = (BASE, BASE + 0x100000, BASE + 0x200000, 16, 32)
     rc, msg = _call_step(lib, [good])
     assert rc == 4 and "MUON_TEST_FAIL_ALLOC" in msg
+
+
+# ---- strided logical-matrix views and the NS element type -----------------
+
+def _call_views(lib, views, dtype=1, opts=None):
+    """views: (param, grad, momentum, rows, cols, ld) with fake aligned addresses."""
+    import newton_schulz_10_amd as nsa
+    arr = (nsa.MatrixView * len(views))(*[nsa.MatrixView(*v) for v in views])
+    rc = lib.muon_step_views(arr, len(views), 0.02, 0.95, 5, dtype,
+                             ctypes.byref(opts) if opts is not None else None, None)
+    return rc, lib.muon_last_error().decode()
+
+
+def test_view_validation(lib, monkeypatch):
+    # With MUON_TEST_FAIL_ALLOC=1 a call that passes validation reports
+    # out-of-memory (4) before touching the device.
+    monkeypatch.setenv("MUON_TEST_FAIL_ALLOC", "1")
+    P, G, M = BASE, BASE + 0x1000000, BASE + 0x2000000
+    # Two interleaved row views of a 64 x 256 bf16 parameter (even / odd
+    # rows, stride 512 elements) with momentum laid out the same way.
+    even = (P, G, M, 32, 256, 512)
+    odd = (P + 512, G + 512, M + 1024, 32, 256, 512)
+    assert _call_views(lib, [even, odd])[0] == 4
+    # The same rows twice.
+    rc, msg = _call_views(lib, [even, (P, G + 0x100000, M + 0x100000, 32, 256, 512)])
+    assert rc == 1 and "overlaps" in msg
+    # Column halves of a 64 x 256 parameter (ld 256, 128 columns each), and
+    # a third view straddling them.
+    left = (P, G, M, 64, 128, 256)
+    right = (P + 256, G + 256, M + 512, 64, 128, 256)
+    assert _call_views(lib, [left, right])[0] == 4
+    mid = (P + 128, G + 0x100000, M + 0x100000, 64, 128, 256)
+    rc, msg = _call_views(lib, [left, right, mid])
+    assert rc == 1 and "params" in msg
+    # ld 0 means contiguous; ld < cols and ld >= 2^31 are rejected.
+    assert _call_views(lib, [(P, G, M, 64, 256, 0)])[0] == 4
+    rc, msg = _call_views(lib, [(P, G, M, 64, 256, 255)])
+    assert rc == 1 and "ld" in msg
+    assert _call_views(lib, [(P, G, M, 64, 256, 1 << 31)])[0] == 1
+    # A grad view that shares columns with its own param view, and one in
+    # the other column half of the same rows (disjoint).
+    assert _call_views(lib, [(P, P + 128, M, 64, 128, 256)])[0] == 1
+    assert _call_views(lib, [(P, P + 256, M, 64, 128, 256)])[0] == 4
+    assert lib.muon_step_views(None, 1, 0.02, 0.95, 5, 1, None, None) == 1
+    assert lib.muon_step_views(None, 0, 0.02, 0.95, 5, 1, None, None) == 0
+
+
+def test_ns_dtype_option(lib, monkeypatch):
+    import newton_schulz_10_amd as nsa
+    monkeypatch.setenv("MUON_TEST_FAIL_ALLOC", "1")
+    good = (BASE, BASE + 0x100000, BASE + 0x200000, 16, 32)
+    o = nsa.Options()
+    lib.muon_default_options(ctypes.byref(o))
+    assert o.ns_dtype == -1
+    o.ns_dtype = 2
+    rc, msg = _call_step(lib, [good], dtype=0, opts=o)
+    assert rc == 1 and "ns_dtype" in msg
+    o.ns_dtype = 1   # fp32 tensors, bf16 NS
+    assert _call_step(lib, [good], dtype=0, opts=o)[0] == 4
+
+
+def test_plan_query_follows_ns_dtype(lib):
+    import torch
+    import newton_schulz_10_amd as nsa
+    f32 = nsa.plan_query([(300, 520)], dtype=torch.float32)
+    mixed = nsa.plan_query([(300, 520)], dtype=torch.float32, ns_dtype=torch.bfloat16)
+    bf = nsa.plan_query([(300, 520)], dtype=torch.bfloat16)
+    # The NS element type sets the padding (fp32: 64; bf16: m to 128, n to 256)
+    # and the workspace layout.
+    assert (f32["batches"][0]["m_pad"], f32["batches"][0]["n_pad"]) == (320, 576)
+    assert (mixed["batches"][0]["m_pad"], mixed["batches"][0]["n_pad"]) == (384, 768)
+    assert mixed["batches"] == bf["batches"] and mixed["workspace_bytes"] == bf["workspace_bytes"]
