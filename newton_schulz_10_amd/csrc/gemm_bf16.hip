@@ -71,6 +71,17 @@ constexpr int BK = 32;               // K per LDS stage
 constexpr int kStages = 4;           // LDS stages (fill runs three slabs ahead)
 constexpr int kStageRows = 640;      // P rows + Q rows of a stage (wide tile: 128 + 512)
 constexpr int kThreads = 256;
+// Tile order within a matrix. Up to kRowMajorMax tile rows (A/B) or tile
+// columns (X') it is row-major: the 32 tiles an XCD runs at once then
+// already form a block of whole short rows. Beyond, tiles go in bands of
+// kGroupRows tile rows, column-major inside a band, so that the tiles run
+// at once share a few row and column panels (a long row-major window
+// would stream most of the operand again for every tile row). Measured on
+// one box: ns_update -14.5% on 4096 x 14336 matrices and -4.5% on the
+// 7168-row stack, and +1.6% on 1408 x 2048 (8 tile columns), where
+// row-major is kept.
+constexpr int kRowMajorMax = 8;
+constexpr int kGroupRows = 4;
 
 // Chunk swizzle of the [row][32 k] stages (64 B rows, 4 chunks of 16 B):
 // chunk index XOR g(row). The fragment reads (ds_read_b128, one row per
@@ -926,9 +937,9 @@ __device__ __forceinline__ void gemm_diag_tile(const GemmArgs& g, int mat, int I
 // schedule (g.sched) it then claims the next unclaimed tile of the range
 // from the XCD's counter (tiles differ in cost: diagonal tiles of A'/B'
 // multiply 36 of 64 blocks), else it takes tiles s + slots, s + 2 slots, ....
-// Tile order within a matrix: full tiles (row-major over the lower triangle
-// for A/B, over all rows x columns for X'), then the wide tiles of the
-// half row.
+// Tile order within a matrix: full tiles (over the lower triangle for A/B,
+// over all rows x columns for X'; row-major or banded, see kRowMajorMax),
+// then the wide tiles of the half row.
 template <int ROLE>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void ns_gemm_bf16(GemmArgs g) {
@@ -960,13 +971,46 @@ void ns_gemm_bf16(GemmArgs g) {
     const int u = t % G.per_mat;
     if (u < G.full) {
       int I, J;
-      if (kSym) {   // lower triangle, row-major: row I holds I + 1 tiles
+      if (kSym && G.F <= kRowMajorMax) {   // lower triangle, row-major: row I holds I + 1 tiles
         I = 0;
         while ((I + 1) * (I + 2) / 2 <= u) ++I;
         J = u - I * (I + 1) / 2;
-      } else {
+      } else if (kSym) {
+        // Lower triangle in bands of kGroupRows tile rows, column-major
+        // inside a band (the full columns J < r0, then the band's own
+        // triangle), so the tiles an XCD runs at once share a few row and
+        // column panels; rows r < r0 hold r0 (r0 + 1) / 2 tiles.
+        int r0 = 0, r1 = kGroupRows < G.F ? kGroupRows : G.F;
+        while (u >= r1 * (r1 + 1) / 2) {
+          r0 = r1;
+          r1 = r0 + kGroupRows < G.F ? r0 + kGroupRows : G.F;
+        }
+        const int gm = r1 - r0;
+        int v = u - r0 * (r0 + 1) / 2;
+        if (v < r0 * gm) {
+          I = r0 + v % gm;
+          J = v / gm;
+        } else {
+          v -= r0 * gm;
+          int c = 0;
+          while (v >= gm - c) { v -= gm - c; ++c; }
+          J = r0 + c;
+          I = J + v;
+        }
+      } else if (G.tn <= kRowMajorMax) {
         I = u / G.tn;
         J = u % G.tn;
+      } else {
+        // Groups of kGroupRows tile rows, column-major inside a group: the
+        // tiles an XCD runs at once form a block of about 4 x 8 tiles that
+        // share 4 row panels of B' and 8 column panels of X. (Row-major,
+        // a wide X would be streamed again for every tile row.)
+        const int gsz = kGroupRows * G.tn;
+        const int r0 = (u / gsz) * kGroupRows;
+        const int gm = G.F - r0 < kGroupRows ? G.F - r0 : kGroupRows;
+        const int v = u - r0 * G.tn;
+        I = r0 + v % gm;
+        J = v / gm;
       }
       if constexpr (kSym) {
         if (I == J && !(ROLE == kPoly && g.poly_operand)) gemm_diag_tile<ROLE>(g, mat, I, lds, cl, next);

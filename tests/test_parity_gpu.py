@@ -89,6 +89,20 @@ def test_ragged_shapes(nsa, dtype, tol):
     _print(dtype, "ragged worst rel err", worst)
 
 
+def test_banded_tile_orders(nsa):
+    # More than 8 tile rows and columns: Gram/Poly tiles go in bands of 4
+    # tile rows and Update tiles in groups of 4 rows, column-major inside
+    # (2304 = 9 tile rows; 2432 = 9.5, with the half row of wide tiles;
+    # 2560 = 10 tile columns).
+    shapes = [(2304, 2560), (2560, 2432)]
+    case = workloads.random_case(16, shapes, "bf16", params_init="zero")
+    _print("banded tile orders", shapes)
+    p1, m1 = run_case(nsa, case, "bf16")
+    ref = oracle_case(case, 0.02, 0.95, 5)
+    worst = assert_parity(case, "bf16", p1, m1, ref, BF16_TOL)
+    _print("banded tile orders worst rel err", worst)
+
+
 def test_fp32_nonzero_params_and_options(nsa):
     shapes = [(96, 160), (160, 96), (64, 64)]
     case = workloads.random_case(2, shapes, "f32")
