@@ -65,6 +65,9 @@ def parse():
                     help="also run one plain 1 GiB device copy (for HBM counter scaling)")
     ap.add_argument("--summarize", nargs=3, metavar=("TRACE_DIR", "FETCH_DIR", "WRITE_DIR"),
                     help="write profiles/ summaries from rocprofv3 csv outputs and exit")
+    ap.add_argument("--mfma", metavar="MFMA_DIR",
+                    help="with --summarize: a --pmc MfmaFlopsBF16 MfmaUtil run, for executed MFMA flops "
+                         "and MFMA busy time per kernel")
     return ap.parse_args()
 
 
@@ -107,8 +110,8 @@ def _read_csvs(d: str, suffix: str):
 
 
 def _counter_per_kind(rows, counter):
-    """Mean counter value (KiB) per dispatch for each library kernel kind,
-    plus the value read for the calibration copy."""
+    """Mean counter value per dispatch for each library kernel kind, plus
+    the value read for the calibration copy."""
     per_dispatch = {}
     for r in rows:
         if r["Counter_Name"] != counter:
@@ -125,8 +128,13 @@ def _counter_per_kind(rows, counter):
     return {k: sum(v) / len(v) for k, v in kinds.items()}, copy
 
 
-def summarize(trace_dir, fetch_dir, write_dir, workload):
+def summarize(trace_dir, fetch_dir, write_dir, workload, mfma_dir=None):
     stats = _read_csvs(trace_dir, "kernel_stats.csv")
+    mflops, mutil = {}, {}
+    if mfma_dir:
+        rows = _read_csvs(mfma_dir, "counter_collection.csv")
+        mflops, _ = _counter_per_kind(rows, "MfmaFlopsBF16")
+        mutil, _ = _counter_per_kind(rows, "MfmaUtil")
     fetch, fcopy = _counter_per_kind(_read_csvs(fetch_dir, "counter_collection.csv"), "FETCH_SIZE")
     write, wcopy = _counter_per_kind(_read_csvs(write_dir, "counter_collection.csv"), "WRITE_SIZE")
     if not fcopy or not wcopy:
@@ -145,6 +153,9 @@ def summarize(trace_dir, fetch_dir, write_dir, workload):
         e["avg_ms"] = e["total_ns"] / e["calls"] / 1e6
         e["hbm_read_bytes_per_launch"] = fetch.get(k, 0.0) * 1024.0 * f_scale if k in fetch else None
         e["hbm_write_bytes_per_launch"] = write.get(k, 0.0) * 1024.0 * w_scale if k in write else None
+        if mfma_dir:
+            e["mfma_bf16_flops_per_launch"] = mflops.get(k)
+            e["mfma_busy_pct"] = mutil.get(k)
     dom = max(kinds, key=lambda k: kinds[k]["total_ns"])
     data = {"workload": workload, "source_sha256": source_hash(),
             "calibration": {"copy_bytes": COPY_CALIB_BYTES, "fetch_kib_read": fcopy, "write_kib_read": wcopy,
@@ -161,15 +172,37 @@ def summarize(trace_dir, fetch_dir, write_dir, workload):
         for c, d in (("FETCH_SIZE", "<FETCH_DIR>"), ("WRITE_SIZE", "<WRITE_DIR>")):
             f.write(f"rocprofv3 --pmc {c} --output-format csv -d {d} -o pmc -- "
                     f"python3 $REPO/bench.py --workload {workload} --steps 1 --warmup 0 --cpu-seconds 0 --copy-calib\n")
-        f.write("python3 $REPO/bench.py --summarize <TRACE_DIR> <FETCH_DIR> <WRITE_DIR>\n```\n\n")
+        if mfma_dir:
+            f.write(f"rocprofv3 --pmc MfmaFlopsBF16 MfmaUtil --output-format csv -d <MFMA_DIR> -o pmc -- "
+                    f"python3 $REPO/bench.py --workload {workload} --steps 1 --warmup 0 --cpu-seconds 0\n")
+            f.write(f"python3 $REPO/bench.py --summarize <TRACE_DIR> <FETCH_DIR> <WRITE_DIR> --mfma <MFMA_DIR> "
+                    f"--workload {workload}\n```\n\n")
+        else:
+            f.write(f"python3 $REPO/bench.py --summarize <TRACE_DIR> <FETCH_DIR> <WRITE_DIR> --workload {workload}\n```\n\n")
         f.write(f"Counter scale: a {COPY_CALIB_BYTES >> 20} MiB device copy reads FETCH_SIZE {fcopy:.0f} KiB "
                 f"(x{f_scale:.3f}) and WRITE_SIZE {wcopy:.0f} KiB (x{w_scale:.3f}).\n\n")
-        f.write("| kernel | launches | avg ms | HBM read GB/launch | HBM write GB/launch |\n|---|---|---|---|---|\n")
+        if mfma_dir:
+            f.write("MFMA columns: executed bf16 MFMA flops per launch (MfmaFlopsBF16, the MFMA op counter x 512), "
+                    "the same over the launch's average duration, and MFMA busy time over GPU-active time "
+                    "summed over all SIMDs (MfmaUtil).\n\n")
+        head = "| kernel | launches | avg ms | HBM read GB/launch | HBM write GB/launch |"
+        rule = "|---|---|---|---|---|"
+        if mfma_dir:
+            head += " executed MFMA TFLOP/launch | executed TFLOP/s | MFMA busy % |"
+            rule += "---|---|---|"
+        f.write(head + "\n" + rule + "\n")
         for k, e in sorted(kinds.items(), key=lambda kv: -kv[1]["total_ns"]):
             rd = e["hbm_read_bytes_per_launch"]
             wr = e["hbm_write_bytes_per_launch"]
-            f.write(f"| {k} | {e['calls']} | {e['avg_ms']:.4f} | "
-                    f"{'-' if rd is None else f'{rd / 1e9:.4f}'} | {'-' if wr is None else f'{wr / 1e9:.4f}'} |\n")
+            line = (f"| {k} | {e['calls']} | {e['avg_ms']:.4f} | "
+                    f"{'-' if rd is None else f'{rd / 1e9:.4f}'} | {'-' if wr is None else f'{wr / 1e9:.4f}'} |")
+            if mfma_dir:
+                fl, ut = e.get("mfma_bf16_flops_per_launch"), e.get("mfma_busy_pct")
+                rate = fl / (e["avg_ms"] * 1e-3) / 1e12 if fl else None
+                line += (f" {'-' if not fl else f'{fl / 1e12:.4f}'} |"
+                         f" {'-' if rate is None else f'{rate:.1f}'} |"
+                         f" {'-' if ut is None else f'{ut:.1f}'} |")
+            f.write(line + "\n")
         f.write("\nMachine-readable copy (bench.py reads it while `source_sha256` matches the sources):\n\n")
         f.write("```json\n" + json.dumps(data, indent=1) + "\n```\n")
     print(out)
@@ -263,7 +296,7 @@ def cpu_baseline(w, budget_s):
 def main():
     args = parse()
     if args.summarize:
-        summarize(*args.summarize, args.workload)
+        summarize(*args.summarize, args.workload, args.mfma)
         return
     if args.gpus != 1:
         print(f"bench.py measures one GPU: --gpus {args.gpus} is not supported (the library runs on "
