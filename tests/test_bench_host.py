@@ -1,0 +1,85 @@
+"""CPU tests of bench.py's host logic: the flop count, the --gpus guard,
+and the rocprofv3 summary (per-kernel durations, HBM bytes scaled by a
+copy of known size, MFMA counters) read back only while the kernel
+sources are unchanged."""
+import csv
+import os
+import subprocess
+import sys
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+sys.path.insert(0, ROOT)
+import bench  # noqa: E402
+
+UPD = "void muon::(anonymous namespace)::ns_gemm_bf16<2>(muon::GemmArgs)"
+GRAM = "void muon::(anonymous namespace)::ns_gemm_bf16<0>(muon::GemmArgs)"
+COPY = "__amd_rocclr_copyBuffer"
+
+
+def _write(path, rows, fields):
+    os.makedirs(os.path.dirname(path), exist_ok=True)
+    with open(path, "w", newline="") as f:
+        w = csv.DictWriter(f, fieldnames=fields)
+        w.writeheader()
+        w.writerows(rows)
+
+
+def _counters(d, name, per_kernel):
+    rows = []
+    for i, (kern, v) in enumerate(per_kernel):
+        rows.append({"Dispatch_Id": i, "Kernel_Name": kern, "Counter_Name": name, "Counter_Value": v})
+    _write(os.path.join(d, "pmc_counter_collection.csv"), rows,
+           ["Dispatch_Id", "Kernel_Name", "Counter_Name", "Counter_Value"])
+
+
+def test_nominal_flops():
+    # per NS iteration 4 m^2 n + 2 m^3 with m <= n, either orientation
+    assert bench.nominal_ns_flops(1408, 2048, 5) == 5 * (4 * 1408 ** 2 * 2048 + 2 * 1408 ** 3)
+    assert bench.nominal_ns_flops(2048, 1408, 5) == bench.nominal_ns_flops(1408, 2048, 5)
+    assert bench.nominal_ns_flops(3, 5, 0) == 0
+
+
+def test_more_than_one_gpu_is_refused():
+    r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"],
+                       capture_output=True, text=True)
+    assert r.returncode == 2 and "one GPU" in r.stderr
+
+
+def test_summary_scales_counters_and_tracks_sources(tmp_path, monkeypatch):
+    monkeypatch.setattr(bench, "PROFILES", str(tmp_path / "profiles"))
+    tr, fe, wr, mf = (str(tmp_path / d) for d in ("trace", "fetch", "write", "mfma"))
+    _write(os.path.join(tr, "trace_kernel_stats.csv"),
+           [{"Name": UPD, "Calls": 4, "TotalDurationNs": 4e6},
+            {"Name": GRAM, "Calls": 4, "TotalDurationNs": 2e6},
+            {"Name": "some_other_kernel", "Calls": 1, "TotalDurationNs": 9e9}],
+           ["Name", "Calls", "TotalDurationNs"])
+    # The copy of 1 GiB reads 0.5 GiB of FETCH_SIZE (scale 2) and 1 GiB of
+    # WRITE_SIZE (scale 1); two Update dispatches average 1000 KiB fetched.
+    _counters(fe, "FETCH_SIZE", [(UPD, 900.0), (UPD, 1100.0), (GRAM, 10.0), (COPY, 524288.0)])
+    _counters(wr, "WRITE_SIZE", [(UPD, 300.0), (GRAM, 20.0), (COPY, 1048576.0)])
+    _counters(mf, "MfmaFlopsBF16", [(UPD, 2e12), (GRAM, 1e12)])
+    with open(os.path.join(mf, "pmc_counter_collection.csv"), "a", newline="") as f:
+        csv.writer(f).writerows([[9, UPD, "MfmaUtil", 55.0], [10, GRAM, "MfmaUtil", 45.0]])
+    bench.summarize(tr, fe, wr, "w_test", mf)
+    out = tmp_path / "profiles" / "ns_update_w_test.md"
+    text = out.read_text()
+    assert "| ns_update | 4 | 1.0000 | 0.0020 | 0.0003 | 2.0000 | 2000.0 | 55.0 |" in text
+    assert "some_other_kernel" not in text
+    got = bench.load_traffic("w_test", "ns_update")
+    assert got == pytest.approx(1000 * 1024 * 2 + 300 * 1024)
+    # A summary taken on other kernel sources is not used.
+    monkeypatch.setattr(bench, "source_hash", lambda: "0000000000000000")
+    assert bench.load_traffic("w_test", "ns_update") is None
+
+
+def test_summary_needs_the_calibration_copy(tmp_path, monkeypatch):
+    monkeypatch.setattr(bench, "PROFILES", str(tmp_path / "profiles"))
+    tr, fe, wr = (str(tmp_path / d) for d in ("trace", "fetch", "write"))
+    _write(os.path.join(tr, "trace_kernel_stats.csv"), [{"Name": UPD, "Calls": 1, "TotalDurationNs": 1e6}],
+           ["Name", "Calls", "TotalDurationNs"])
+    _counters(fe, "FETCH_SIZE", [(UPD, 1.0)])
+    _counters(wr, "WRITE_SIZE", [(UPD, 1.0)])
+    with pytest.raises(SystemExit):
+        bench.summarize(tr, fe, wr, "w_test")
