@@ -208,8 +208,8 @@ def summarize(trace_dir, fetch_dir, write_dir, workload, mfma_dir=None):
     print(out)
 
 
-def load_traffic(workload, kind):
-    """HBM bytes per launch of `kind` from the committed summary, or None
+def load_summary(workload, kind):
+    """The committed rocprofv3 summary's entry for kernel `kind`, or None
     when there is none or it was taken on other kernel sources."""
     for p in glob.glob(os.path.join(PROFILES, f"*_{workload}.md")):
         with open(p) as f:
@@ -220,9 +220,37 @@ def load_traffic(workload, kind):
         if data.get("source_sha256") != source_hash():
             continue
         e = data["kernels"].get(kind)
-        if e and e.get("hbm_read_bytes_per_launch") is not None and e.get("hbm_write_bytes_per_launch") is not None:
-            return e["hbm_read_bytes_per_launch"] + e["hbm_write_bytes_per_launch"]
+        if e:
+            return e
     return None
+
+
+def load_traffic(workload, kind):
+    """HBM bytes per launch of `kind` from the committed summary, or None
+    when there is none or it was taken on other kernel sources."""
+    e = load_summary(workload, kind)
+    if e and e.get("hbm_read_bytes_per_launch") is not None and e.get("hbm_write_bytes_per_launch") is not None:
+        return e["hbm_read_bytes_per_launch"] + e["hbm_write_bytes_per_launch"]
+    return None
+
+
+def environment():
+    """Versions and hardware the numbers were taken on."""
+    import torch
+    env = {"torch": torch.__version__, "hip": getattr(torch.version, "hip", None)}
+    try:
+        p = torch.cuda.get_device_properties(0)
+        env["gpu"] = p.name
+        env["gcn_arch"] = getattr(p, "gcnArchName", None)
+        env["compute_units"] = p.multi_processor_count
+    except Exception:  # pragma: no cover
+        pass
+    try:
+        with open("/proc/cpuinfo") as f:
+            env["cpu"] = next((l.split(":", 1)[1].strip() for l in f if l.startswith("model name")), None)
+    except OSError:  # pragma: no cover
+        pass
+    return env
 
 
 # --------------------------------------------------------------------------
@@ -361,6 +389,12 @@ def main():
                 "traffic": traffic, "kernel": dom, "flops_per_launch": live_flops / dv["launches"],
                 "flops_counted": "live matrices (idle experts excluded)",
                 "avg_launch_ms": avg_launch_ms}
+        summ = load_summary(w.key, dom)
+        if summ and summ.get("mfma_bf16_flops_per_launch"):
+            # From the committed counter run on the same sources: executed
+            # MFMA flops per launch and MFMA busy time (rocprofv3).
+            roof["executed_mfma_tflop_per_launch"] = summ["mfma_bf16_flops_per_launch"] / 1e12
+            roof["mfma_busy_pct"] = summ.get("mfma_busy_pct")
     else:
         achieved = dv["bytes"] / (dv["total_ms"] * 1e-3) / 1e9
         roof = {"bound": "hbm", "achieved": achieved, "peak": PEAK_HBM_GBS, "unit": "GB/s",
@@ -398,6 +432,7 @@ def main():
         "roofline": roof,
         "kernels": per_kernel,
         "cpu_baseline": cpu,
+        "env": environment(),
     }
     print(json.dumps(out), flush=True)
 

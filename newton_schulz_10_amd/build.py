@@ -68,7 +68,7 @@ def build_library(verbose: bool = False) -> str:
         objs = list(ex.map(lambda s: _compile(s, verbose), SOURCES))
     tmp = LIB + ".tmp"
     cmd = [hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp] + objs + \
-          ["-Wl,-soname,libmuon.so", "-Wl,-rpath,/opt/rocm/lib"]
+          ["-L/opt/rocm/lib", "-lrocprofiler-sdk-roctx", "-Wl,-soname,libmuon.so", "-Wl,-rpath,/opt/rocm/lib"]
     if verbose:
         print(" ".join(cmd), flush=True)
     r = subprocess.run(cmd, capture_output=True, text=True)

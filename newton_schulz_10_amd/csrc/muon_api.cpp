@@ -12,6 +12,7 @@
 //   ns_steps x { gram, poly, update }          -> X_k (s_i folded into step 1)
 //   apply      (per chunk)                     -> p' (or out)
 #include <hip/hip_runtime.h>
+#include <rocprofiler-sdk-roctx/roctx.h>
 
 #include <algorithm>
 #include <cmath>
@@ -111,6 +112,17 @@ struct ProfScope {
   }
 };
 
+// ---- named host ranges ------------------------------------------------------
+
+// A roctx range around a phase of the call (shown by `rocprofv3
+// --marker-trace`; a no-op when no tool is attached). Popped on every exit.
+struct PhaseRange {
+  explicit PhaseRange(const std::string& name) { roctxRangePushA(name.c_str()); }
+  ~PhaseRange() { roctxRangePop(); }
+  PhaseRange(const PhaseRange&) = delete;
+  PhaseRange& operator=(const PhaseRange&) = delete;
+};
+
 // ---- the launch sequence --------------------------------------------------
 
 struct MatRef {
@@ -150,6 +162,8 @@ int fit_units(const muon_options& o) {
 int run(const std::vector<MatRef>& mats, float lr, float beta, int ns_steps, muon_dtype dtype,
         const muon_options& o, bool orthogonalize_only, hipStream_t stream) {
   if (mats.empty()) return MUON_OK;
+  PhaseRange call_range(std::string(orthogonalize_only ? "muon_orthogonalize" : "muon_step") + " (" +
+                   std::to_string(mats.size()) + " matrices)");
   const int num = (int)mats.size();
   std::vector<int> rows(num), cols(num);
   for (int i = 0; i < num; ++i) { rows[i] = mats[i].rows; cols[i] = mats[i].cols; }
@@ -186,6 +200,8 @@ int run(const std::vector<MatRef>& mats, float lr, float beta, int ns_steps, muo
   int status = MUON_OK;
 
   for (const Batch& B : plan.batches) {
+    PhaseRange batch_range("batch: " + std::to_string(B.count) + " x " + std::to_string(B.m) + "x" +
+                      std::to_string(B.n) + " (group " + std::to_string(B.group) + ")");
     const Layout L = batch_layout(B.count, B.m_pad, B.n_pad, ns);
     void* x0 = W + L.x0;
     void* x1 = W + L.x1;
@@ -254,6 +270,7 @@ int run(const std::vector<MatRef>& mats, float lr, float beta, int ns_steps, muo
     void* X = x0;
     void* Xn = x1;
     for (int k = 0; k < ns_steps && status == MUON_OK; ++k) {
+      PhaseRange step_range("ns step " + std::to_string(k + 1));
       GemmArgs g{};
       g.mat_x = L.mat_x; g.mat_a = L.mat_a; g.count = B.count;
       g.m = B.m; g.n = B.n; g.m_pad = B.m_pad; g.n_pad = B.n_pad;

@@ -325,6 +325,33 @@ def test_non_default_stream(nsa):
     assert all(torch.equal(a, b) for a, b in zip(P, P2))
 
 
+def test_call_does_not_synchronize_the_device(nsa):
+    # A bounded spin kernel on one stream is still running when a call on
+    # another stream has returned: the call only enqueues work (no device
+    # or stream synchronisation), and its results are right once its own
+    # stream is synchronised.
+    import torch
+    case = workloads.random_case(13, [(256, 384), (384, 256)], "bf16")
+    P, G, M = upload_case(case, "bf16")
+    Pw, Gw, Mw = upload_case(case, "bf16")
+    nsa.muon_step(list(zip(Pw, Gw, Mw)), 0.02, 0.95, 5)   # loads the kernels once
+    torch.cuda.synchronize()
+    busy, s = torch.cuda.Stream(), torch.cuda.Stream()
+    done = torch.cuda.Event()
+    with torch.cuda.stream(busy):
+        torch.cuda._sleep(1 << 30)   # about half a second of spinning, then it ends
+        done.record()
+    with torch.cuda.stream(s):
+        nsa.muon_step(list(zip(P, G, M)), 0.02, 0.95, 5)
+    still_running = not done.query()
+    s.synchronize()
+    torch.cuda.synchronize()
+    assert still_running
+    p1 = [from_device(p) for p in P]
+    m1 = [from_device(m) for m in M]
+    assert_parity(case, "bf16", p1, m1, oracle_case(case, 0.02, 0.95, 5), BF16_TOL)
+
+
 def test_alloc_failure_leaves_state_unchanged(nsa, monkeypatch):
     import torch
     case = workloads.random_case(13, [(128, 256)], "bf16")
