@@ -160,3 +160,26 @@ def test_views_against_oracle(nsa):
         e = check_update(p0, from_device(a), rp, "bf16", BF16_TOL)
         assert e <= BF16_TOL, (p0.shape, e)
         assert rel_fro(from_device(c), rb.astype(np.float32)) <= MOM_TOL
+
+
+def test_views_at_model_shapes(nsa):
+    # Real shapes through the fused apply with a row stride other than the
+    # view's width: a fused QKV projection (three 2048 x 2048 heads, ld =
+    # 2048), an expert FC1 with gate/up rows interleaved (two 1408 x 2048
+    # views, ld = 4096) and a tall weight split into column blocks (two
+    # 2048 x 1408 views, ld = 2816). Bitwise equal to contiguous copies.
+    import torch
+    layouts = [((6144, 2048), [np.s_[0:2048], np.s_[2048:4096], np.s_[4096:6144]]),
+               ((2816, 2048), [np.s_[0::2], np.s_[1::2]]),
+               ((2048, 2816), [np.s_[:, 0:1408], np.s_[:, 1408:2816]])]
+    views = []
+    for k, (shape, idx) in enumerate(layouts):
+        p, g, m = _physical(nsa, 70 + k, shape, "bf16")
+        views += [(p[ix], g[ix], m[ix]) for ix in idx]
+    _print("model-shape views", [(tuple(v[0].shape), v[0].stride()) for v in views])
+    copies = [(v[0].contiguous(), v[1].contiguous(), v[2].contiguous()) for v in views]
+    nsa.muon_step_views(views, 0.02, 0.95, 5)
+    nsa.muon_step(copies, 0.02, 0.95, 5)
+    torch.cuda.synchronize()
+    for j, (v, c) in enumerate(zip(views, copies)):
+        assert torch.equal(v[0], c[0]) and torch.equal(v[2], c[2]), (j, tuple(v[0].shape))
