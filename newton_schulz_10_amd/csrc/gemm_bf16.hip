@@ -254,7 +254,7 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& g, int mat, int I, int
   const int last = nk - 1;
   static_assert(PR % 64 == 0, "P rows take whole rounds of the four waves' loads");
   auto fill_one = [&](int kt, int q) {
-    const int k0 = (kt < last ? kt : last) * BK;   // past the end: repeat the last slab
+    const int k0 = kt * BK;   // kt <= last
     const int rb = (q * 4 + wave) * 16;
     const bf16_t* src;
     if (q < PR / 64) {   // rb < PR, decided at compile time
@@ -329,9 +329,9 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& g, int mat, int I, int
   // compute issues fill(j+3) in two halves around its barrier:
   //   fillA(j+3) | barrier j | fillB(j+3).
   // At barrier j the fill of slab j+1 must have landed; the loads issued
-  // after it are fill(j+2) and fillA(j+3): NL + NLh. Fills past the last
-  // slab repeat the last slab (into a stage that is no longer read), which
-  // keeps that count exact to the end.
+  // after it are fill(j+2) and fillA(j+3): NL + NLh. There is no fill past
+  // the last slab, so the last two barriers wait for NL and 0 (slab modes
+  // below).
   for (int j = 0; j < kStages - 1; ++j)
     for (int q = 0; q < NL; ++q) fill_one(j, q);
   __builtin_amdgcn_s_waitcnt(vmcnt(2 * NL));  // fill(0) landed
@@ -363,26 +363,32 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& g, int mat, int I, int
     for (int q = 0; q < NLh; ++q)
       if (8 + (8 * q) / NLh == i) fill_one(kt, h * NLh + q);
   };
-  // One K-slab (two 16-deep steps). `more` (compile-time) says whether a
-  // next slab exists; the last slab is peeled so the loop body has no
-  // data-dependent branch around LDS reads (the compiler's wait-count
-  // bookkeeping then stays exact). Every read of a stage is issued and
-  // completed (lgkmcnt(0)) before the barrier after which that stage is
-  // filled again.
-  auto slab = [&](int kt, auto more) {
-    if constexpr (decltype(more)::value) {
+  // One K-slab (two 16-deep steps). The mode (compile-time) peels the end
+  // of the K loop, so the loop body has no data-dependent branch around LDS
+  // reads and every wait count is exact:
+  //   0: fills slab kt+3; at the barrier fill(kt+2) and fillA(kt+3) may
+  //      still be in flight;
+  //   1: kt = last-2, no fill (there is no slab kt+3); fill(last) may be in
+  //      flight;
+  //   2: kt = last-1, no fill; nothing may be in flight;
+  //   3: the last slab, no barrier.
+  // Every read of a stage is issued and completed (lgkmcnt(0)) before the
+  // barrier after which that stage is filled again.
+  auto slab = [&](int kt, auto mode) {
+    constexpr int M = decltype(mode)::value;
+    if constexpr (M < 3) {
       mfma_step(0, [&](int i) {
         if (i < 8) read_one(kt, 1, i, rf[1], cf[1]);
-        fill_slot(kt + 3, 0, i);
+        if constexpr (M == 0) fill_slot(kt + 3, 0, i);
       });
       // This wave's fill of slab kt+1 and its LDS reads have completed;
       // after the barrier, every wave's have, and stage (kt+3) % 4's last
       // readers (slab kt-1) are long done.
-      __builtin_amdgcn_s_waitcnt(vmcnt_lgkm0(NL + NLh));
+      __builtin_amdgcn_s_waitcnt(vmcnt_lgkm0(M == 0 ? NL + NLh : (M == 1 ? NL : 0)));
       lds_barrier();
       mfma_step(1, [&](int i) {
         if (i < 8) read_one(kt + 1, 0, i, rf[0], cf[0]);
-        fill_slot(kt + 3, 1, i);
+        if constexpr (M == 0) fill_slot(kt + 3, 1, i);
       });
     } else {
       mfma_step(0, [&](int i) {
@@ -391,9 +397,12 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& g, int mat, int I, int
       mfma_step(1, [](int) {});
     }
   };
-  for (int kt = 0; kt < last; ++kt) slab(kt, std::true_type{});
+  // K >= 128 (m_pad is a positive multiple of 128), so nk >= 4.
+  for (int kt = 0; kt < last - 2; ++kt) slab(kt, std::integral_constant<int, 0>{});
+  slab(last - 2, std::integral_constant<int, 1>{});
+  slab(last - 1, std::integral_constant<int, 2>{});
   const int claim = claim_issue(cl, tid);
-  slab(last, std::false_type{});
+  slab(last, std::integral_constant<int, 3>{});
 
   // ---- epilogue ----------------------------------------------------------
   {
@@ -737,7 +746,7 @@ __device__ __forceinline__ void gemm_diag_tile(const GemmArgs& g, int mat, int I
   // Stage rows 0-255 hold the tile's 256 rows ([row][32 k], chunks swizzled
   // by kswz); load q of a wave fills rows (4q + wave)*16 .. +15.
   auto fill_one = [&](int kt, int q) {
-    const int k0 = (kt < last ? kt : last) * BK;   // past the end: repeat the last slab
+    const int k0 = kt * BK;   // kt <= last
     const int rb = (q * 4 + wave) * 16;
     const int r = rb + (lane >> 2);
     dma16(P + (size_t)r * K + k0 + ((lane & 3) ^ kswz(r)) * 8, &lds[kt & (kStages - 1)][rb * BK]);
@@ -798,17 +807,20 @@ __device__ __forceinline__ void gemm_diag_tile(const GemmArgs& g, int mat, int I
       for (int q = 0; q < NLh; ++q)
         if (NR + q == i) fill_one(kt, h * NLh + q);
     };
-    auto slab = [&](int kt, auto more) {
-      if constexpr (decltype(more)::value) {
+    // Modes as in gemm_tile: 0 fills slab kt+3, 1 and 2 (kt = last-2,
+    // last-1) fill nothing and wait for fewer loads, 3 is the last slab.
+    auto slab = [&](int kt, auto mode) {
+      constexpr int M = decltype(mode)::value;
+      if constexpr (M < 3) {
         mstep(0, [&](int i) {
           if (i < NR) read_one(kt, 1, i, rf[1], cf[1]);
-          fill_slot(kt + 3, 0, i);
+          if constexpr (M == 0) fill_slot(kt + 3, 0, i);
         });
-        __builtin_amdgcn_s_waitcnt(vmcnt_lgkm0(NL + NLh));
+        __builtin_amdgcn_s_waitcnt(vmcnt_lgkm0(M == 0 ? NL + NLh : (M == 1 ? NL : 0)));
         lds_barrier();
         mstep(1, [&](int i) {
           if (i < NR) read_one(kt + 1, 0, i, rf[0], cf[0]);
-          fill_slot(kt + 3, 1, i);
+          if constexpr (M == 0) fill_slot(kt + 3, 1, i);
         });
       } else {
         mstep(0, [&](int i) {
@@ -817,9 +829,11 @@ __device__ __forceinline__ void gemm_diag_tile(const GemmArgs& g, int mat, int I
         mstep(1, [](int) {});
       }
     };
-    for (int kt = 0; kt < last; ++kt) slab(kt, std::true_type{});
+    for (int kt = 0; kt < last - 2; ++kt) slab(kt, std::integral_constant<int, 0>{});
+    slab(last - 2, std::integral_constant<int, 1>{});
+    slab(last - 1, std::integral_constant<int, 2>{});
     claim = claim_issue(cl, tid);
-    slab(last, std::false_type{});
+    slab(last, std::integral_constant<int, 3>{});
 
     __builtin_amdgcn_s_waitcnt(0x0070);  // vmcnt(0) lgkmcnt(0): stages no longer read
     lds_barrier();
