@@ -48,6 +48,9 @@
  *     MUON_* status; muon_last_error() gives a message naming the argument
  *     and matrix index (thread-local). Device faults surface at the caller's
  *     next synchronisation. No C++ exception crosses this interface.
+ *   - Environment: MUON_BATCH_CAP=<elements> replaces the default batch cap
+ *     (used when options are NULL or batch_cap_elems is 0); MUON_PROFILE=1
+ *     turns the per-launch timing of muon_profile_enable on from the start.
  *   - Numerics: bf16 matrices are iterated in bf16 with fp32 MFMA
  *     accumulation; each GEMM's epilogue (scale, b*A + c*acc, a*X + acc) is
  *     formed in fp32 and rounded once to bf16 (round to nearest even). The
@@ -102,6 +105,7 @@ typedef struct muon_options {
                              NULL for (3.4445,-4.7750,2.0315) at every step
                              (section 6.2: per-step coefficient sets)           */
   size_t batch_cap_elems; /* max sum of rows*cols per fused batch; 0 => 2^29
+                             (or MUON_BATCH_CAP from the environment)
                              (section 6.6: memory-safe batching). A matrix larger
                              than the cap runs in a batch of its own.            */
   int compute_units;      /* bf16: the balanced split of a shape group into

@@ -81,6 +81,13 @@ struct ProfTotal { int launches = 0; double ms = 0, flops = 0, bytes = 0; };
 
 std::mutex g_prof_mu;
 bool g_prof_on = false;
+// MUON_PROFILE=1 in the environment turns the per-launch timing on from the
+// start (as muon_profile_enable(1) would).
+const bool g_prof_env = [] {
+  const char* v = std::getenv("MUON_PROFILE");
+  if (v && v[0] == '1') g_prof_on = true;
+  return true;
+}();
 std::vector<Pending> g_pending;
 std::vector<hipEvent_t> g_free_events;
 std::map<std::string, ProfTotal> g_totals;
@@ -353,16 +360,25 @@ int run(const std::vector<MatRef>& mats, float lr, float beta, int ns_steps, muo
   return status;
 }
 
+// Batch cap used when the caller leaves it at 0 (or passes no options):
+// MUON_BATCH_CAP from the environment if it is a positive integer, else 2^29.
+size_t default_batch_cap() {
+  if (const char* v = std::getenv("MUON_BATCH_CAP")) {
+    char* end = nullptr;
+    const unsigned long long c = std::strtoull(v, &end, 10);
+    if (end != v && *end == '\0' && c > 0) return (size_t)c;
+  }
+  return MUON_DEFAULT_BATCH_CAP;
+}
+
 int validate_common(float lr, float beta, int ns_steps, muon_dtype dtype, const muon_options* opts,
                     muon_options& o) {
   std::string err;
   int rc = check_scalars(lr, beta, ns_steps, dtype, err);
   if (rc) return fail(rc, err);
   default_options(o);
-  if (opts) {
-    o = *opts;
-    if (o.batch_cap_elems == 0) o.batch_cap_elems = MUON_DEFAULT_BATCH_CAP;
-  }
+  if (opts) o = *opts;
+  if (!opts || o.batch_cap_elems == 0) o.batch_cap_elems = default_batch_cap();
   rc = check_options(o, ns_steps, err);
   if (rc) return fail(rc, err);
   return MUON_OK;
@@ -519,6 +535,7 @@ int muon_plan_query(const int* rows, const int* cols, int num, muon_dtype dtype,
     muon_options o;
     default_options(o);
     if (opts) o = *opts;
+    if (!opts || o.batch_cap_elems == 0) o.batch_cap_elems = default_batch_cap();
     Plan plan;
     std::string err;
     if (o.compute_units < -1) return fail(MUON_ERR_INVALID_ARGUMENT, "options.compute_units must be >= -1");

@@ -6,6 +6,7 @@ import os
 import re
 import shutil
 import subprocess
+import sys
 
 import pytest
 
@@ -269,3 +270,22 @@ def test_plan_query_follows_ns_dtype(lib):
     assert (f32["batches"][0]["m_pad"], f32["batches"][0]["n_pad"]) == (320, 576)
     assert (mixed["batches"][0]["m_pad"], mixed["batches"][0]["n_pad"]) == (384, 768)
     assert mixed["batches"] == bf["batches"] and mixed["workspace_bytes"] == bf["workspace_bytes"]
+
+
+def test_environment_switches(lib, monkeypatch):
+    import newton_schulz_10_amd as nsa
+    shapes = [(2048, 1408)] * 256 + [(1408, 2048)] * 256
+    # MUON_BATCH_CAP replaces the default cap (options NULL or cap 0) ...
+    assert len(nsa.plan_query(shapes)["batches"]) == 3
+    monkeypatch.setenv("MUON_BATCH_CAP", str(64 * 1408 * 2048))
+    assert [b["count"] for b in nsa.plan_query(shapes)["batches"]] == [64] * 8
+    # ... but not an explicit cap, and malformed values are ignored.
+    assert len(nsa.plan_query(shapes, batch_cap_elems=1 << 30)["batches"]) == 2
+    monkeypatch.setenv("MUON_BATCH_CAP", "12abc")
+    assert len(nsa.plan_query(shapes)["batches"]) == 3
+    # MUON_PROFILE=1 turns the per-launch timing on when the library loads.
+    code = ("import newton_schulz_10_amd as m; L = m.load(); "
+            "print(L.muon_profile_enable(0), L.muon_profile_enable(0))")
+    env = dict(os.environ, MUON_PROFILE="1")
+    r = subprocess.run([sys.executable, "-c", code], capture_output=True, text=True, env=env, cwd=ROOT)
+    assert r.stdout.split() == ["1", "0"], r.stdout + r.stderr
