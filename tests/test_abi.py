@@ -289,3 +289,40 @@ def test_environment_switches(lib, monkeypatch):
     env = dict(os.environ, MUON_PROFILE="1")
     r = subprocess.run([sys.executable, "-c", code], capture_output=True, text=True, env=env, cwd=ROOT)
     assert r.stdout.split() == ["1", "0"], r.stdout + r.stderr
+
+
+def test_view_overlap_check_against_brute_force(lib, monkeypatch):
+    # Random small strided views of one bf16 parameter, validated through
+    # muon_step_views (MUON_TEST_FAIL_ALLOC=1: a call that passes validation
+    # returns 4 before touching the device). Expected: rejection (1) iff two
+    # views share a byte, or two views with different strides have
+    # intersecting spans (the documented conservative rule).
+    import numpy as np
+    monkeypatch.setenv("MUON_TEST_FAIL_ALLOC", "1")
+    rng = np.random.default_rng(7)
+    P, G, M = BASE, BASE + 0x1000000, BASE + 0x2000000
+    for trial in range(400):
+        nv = int(rng.integers(2, 4))
+        views, spans = [], []
+        shared_ld = 8 * int(rng.integers(3, 6)) if rng.random() < 0.6 else None   # interleaving views
+        for k in range(nv):
+            rows = int(rng.integers(1, 5))
+            cols = 8 * int(rng.integers(1, 4))
+            ld = max(shared_ld, cols) if shared_ld else cols + 8 * int(rng.integers(0, 3))
+            off = 8 * int(rng.integers(0, 24))           # elements; 16-byte aligned
+            views.append((P + 2 * off, G + 0x10000 * (k + 1), M + 0x40000 * (k + 1), rows, cols, ld))
+            b = set()
+            for r in range(rows):
+                start = 2 * (off + r * ld)
+                b.update(range(start, start + 2 * cols))
+            spans.append((2 * off, 2 * (off + (rows - 1) * ld + cols), ld, b))
+        expect_bad = False
+        for i in range(nv):
+            for j in range(i + 1, nv):
+                (lo1, hi1, ld1, b1), (lo2, hi2, ld2, b2) = spans[i], spans[j]
+                if b1 & b2:
+                    expect_bad = True
+                elif ld1 != ld2 and lo1 < hi2 and lo2 < hi1:
+                    expect_bad = True
+        rc, msg = _call_views(lib, views)
+        assert rc == (1 if expect_bad else 4), (trial, views, msg)
