@@ -89,6 +89,20 @@ def test_ragged_shapes(nsa, dtype, tol):
     _print(dtype, "ragged worst rel err", worst)
 
 
+@pytest.mark.parametrize("dtype,tol", [("bf16", BF16_TOL), ("f32", F32_TOL)])
+def test_random_shapes(nsa, dtype, tol):
+    # A seeded sweep of shapes in [1, 900]^2 (both orientations, every
+    # padding remainder and tile geometry that small sizes reach), one call.
+    rng = np.random.default_rng(2024)
+    shapes = [(int(r), int(c)) for r, c in rng.integers(1, 901, size=(20, 2))]
+    case = workloads.random_case(17, shapes, dtype, params_init="zero")
+    _print("random shapes", dtype, shapes)
+    p1, m1 = run_case(nsa, case, dtype)
+    ref = oracle_case(case, 0.02, 0.95, 5)
+    worst = assert_parity(case, dtype, p1, m1, ref, tol)
+    _print(dtype, "random shapes worst rel err", worst)
+
+
 def test_banded_tile_orders(nsa):
     # More than 8 tile rows and columns: Gram/Poly tiles go in bands of 4
     # tile rows and Update tiles in groups of 4 rows, column-major inside

@@ -183,3 +183,23 @@ def test_views_at_model_shapes(nsa):
     torch.cuda.synchronize()
     for j, (v, c) in enumerate(zip(views, copies)):
         assert torch.equal(v[0], c[0]) and torch.equal(v[2], c[2]), (j, tuple(v[0].shape))
+
+
+def test_views_of_fp32_masters_with_bf16_ns(nsa):
+    # Strided views of fp32 master parameters iterated on bf16 MFMA: bitwise
+    # the contiguous result, and within the bf16 bar of the oracle.
+    import torch
+    p, g, m = _physical(nsa, 80, (768, 512), "f32")
+    vs = [(p[0::2], g[0::2], m[0::2]), (p[1::2, 0:256], g[1::2, 0:256], m[1::2, 0:256])]
+    before = [(from_device(a), from_device(b), from_device(c)) for a, b, c in vs]
+    copies = [(a.contiguous(), b.contiguous(), c.contiguous()) for a, b, c in vs]
+    nsa.muon_step_views(vs, 0.02, 0.95, 5, ns_dtype=torch.bfloat16)
+    nsa.muon_step(copies, 0.02, 0.95, 5, ns_dtype=torch.bfloat16)
+    torch.cuda.synchronize()
+    import oracle
+    for (p0, g0, m0), (a, _, c), (ca, _, cc) in zip(before, vs, copies):
+        assert torch.equal(a, ca) and torch.equal(c, cc)
+        rp, rb, _ = oracle.muon_matrix_step(p0, g0, m0, 0.02, 0.95, 5)
+        e = check_update(p0, from_device(a), rp, "f32", BF16_TOL)
+        assert e <= BF16_TOL, (p0.shape, e)
+        assert rel_fro(from_device(c), rb.astype(np.float32)) <= MOM_TOL
