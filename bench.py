@@ -57,10 +57,12 @@ KERNEL_NAMES = {  # rocprofv3 kernel name fragment -> library kernel kind
 def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=10)
-    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--steps", type=int, default=30)
+    ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="moe_bank_2048x1408")
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="oracle sample budget (0 = skip)")
+    ap.add_argument("--poly-form", default="square", choices=["square", "direct"],
+                    help="bf16 form of the NS polynomial step (muon_options.poly_form)")
     ap.add_argument("--copy-calib", action="store_true",
                     help="also run one plain 1 GiB device copy (for HBM counter scaling)")
     ap.add_argument("--summarize", nargs=3, metavar=("TRACE_DIR", "FETCH_DIR", "WRITE_DIR"),
@@ -86,6 +88,105 @@ def nominal_ns_flops(rows: int, cols: int, ns_steps: int) -> int:
     (2 m^3) and B X (2 m^2 n), with m <= n after the transpose-first rule."""
     m, n = min(rows, cols), max(rows, cols)
     return ns_steps * (4 * m * m * n + 2 * m ** 3)
+
+
+def executed_mfma_flops(rows: int, cols: int, ns_steps: int, poly_form: str = "square") -> dict:
+    """bf16 MFMA flops the GEMM kernels execute for one matrix, per kernel
+    kind, from their tile geometry: m padded to 128 and n to 256 (m <= n);
+    256 x 256 tiles, plus 128 x 512 tiles over the half tile row when m_pad
+    is an odd multiple of 128; Gram and Poly over the lower triangle of
+    tiles, diagonal tiles multiplying 36 of their 64 blocks of 32 x 32
+    (Poly's only when no epilogue reads an operand tile, i.e. the square
+    form); Update over every tile of X'."""
+    m, n = min(rows, cols), max(rows, cols)
+    mp, np_ = -(-m // 128) * 128, -(-n // 256) * 256
+    F, half = mp // 256, mp % 256 != 0
+    full_tile, wide_tile = 2 * 256 * 256, 2 * 128 * 512   # flops per unit K
+    ts = F + half
+    wide_sym = (ts + 1) // 2 if half else 0
+    tu = np_ // 256
+    wide_upd = (tu + 1) // 2 if half else 0
+
+    def sym(K, diag_frac):
+        return (F * (F - 1) // 2 * full_tile + F * diag_frac * full_tile + wide_sym * wide_tile) * K
+
+    gram = sym(np_, 36 / 64)
+    poly = sym(mp, 36 / 64 if poly_form == "square" else 1.0)
+    upd = (F * tu * full_tile + wide_upd * wide_tile) * mp
+    return {"ns_gram": ns_steps * gram, "ns_poly": ns_steps * poly, "ns_update": ns_steps * upd}
+
+
+class ClockSampler:
+    """Samples the GPU's GFX clock (MHz) and socket power (W) from the host
+    with amdsmi in a background thread; summary() gives their means over the
+    samples taken between start() and stop()."""
+
+    def __init__(self, period_s: float = 0.01):
+        self.period = period_s
+        self.samples = []
+        self.error = None
+        self._stop = None
+        self._thread = None
+        self._h = None
+        try:
+            import amdsmi
+            self._smi = amdsmi
+            amdsmi.amdsmi_init()
+            handles = amdsmi.amdsmi_get_processor_handles()
+            self._h = handles[0] if handles else None
+            try:
+                import torch
+                bus = torch.cuda.get_device_properties(0).pci_bus_id
+                for h in handles:
+                    if int(amdsmi.amdsmi_get_gpu_device_bdf(h).split(":")[1], 16) == bus:
+                        self._h = h
+            except Exception:  # pragma: no cover
+                pass
+        except Exception as e:  # pragma: no cover
+            self.error = f"{type(e).__name__}: {e}"
+
+    def _read(self):
+        smi = self._smi
+        clk = smi.amdsmi_get_clock_info(self._h, smi.AmdSmiClkType.GFX)["clk"]
+        pw = smi.amdsmi_get_power_info(self._h)
+        w = pw.get("current_socket_power", "N/A")
+        if not isinstance(w, (int, float)):
+            w = pw.get("average_socket_power", None)
+        return float(clk), (float(w) if isinstance(w, (int, float)) else None)
+
+    def start(self):
+        import threading
+        if self._h is None:
+            return
+        self._stop = threading.Event()
+
+        def loop():
+            while not self._stop.is_set():
+                try:
+                    self.samples.append(self._read())
+                except Exception as e:  # pragma: no cover
+                    self.error = f"{type(e).__name__}: {e}"
+                    return
+                self._stop.wait(self.period)
+
+        self._thread = threading.Thread(target=loop, daemon=True)
+        self._thread.start()
+
+    def stop(self):
+        if self._thread is not None:
+            self._stop.set()
+            self._thread.join()
+
+    def summary(self):
+        if not self.samples:
+            return {"sclk_mhz": None, "samples": 0, "error": self.error}
+        clk = [c for c, _ in self.samples]
+        pw = [p for _, p in self.samples if p is not None]
+        out = {"sclk_mhz_mean": sum(clk) / len(clk), "sclk_mhz_min": min(clk), "sclk_mhz_max": max(clk),
+               "samples": len(clk), "source": "amdsmi GFX clock, sampled every 10 ms during the timed steps"}
+        if pw:
+            out["socket_power_w_mean"] = sum(pw) / len(pw)
+        return out
 
 
 def kernel_kind(name: str):
@@ -247,9 +348,22 @@ def environment():
         pass
     try:
         with open("/proc/cpuinfo") as f:
-            env["cpu"] = next((l.split(":", 1)[1].strip() for l in f if l.startswith("model name")), None)
+            info = {}
+            for line in f:
+                if ":" in line:
+                    k, v = line.split(":", 1)
+                    info.setdefault(k.strip(), v.strip())
+        env["cpu"] = info.get("model name")
+        env["cpu_family_model_stepping"] = "/".join(str(info.get(k)) for k in ("cpu family", "model", "stepping"))
+        env["host_cores_visible"] = len(os.sched_getaffinity(0))
     except OSError:  # pragma: no cover
         pass
+    try:
+        from threadpoolctl import threadpool_info
+        env["blas"] = [{k: i.get(k) for k in ("internal_api", "version", "num_threads", "architecture")}
+                       for i in threadpool_info() if i.get("user_api") == "blas"]
+    except Exception as e:  # pragma: no cover
+        env["blas"] = f"unknown ({type(e).__name__})"
     return env
 
 
@@ -350,7 +464,7 @@ def main():
     live_frac = live_flops_per_step / flops_per_step if flops_per_step else 1.0
 
     def step():
-        nsa.muon_step(banks, w.lr, w.beta, w.ns_steps)
+        nsa.muon_step(banks, w.lr, w.beta, w.ns_steps, poly_form=args.poly_form)
 
     for _ in range(args.warmup):
         step()
@@ -360,7 +474,9 @@ def main():
     nsa.profile_enable(True)
     nsa.profile_read(reset=True)
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    clock = ClockSampler()
     torch.cuda.synchronize()
+    clock.start()
     t0 = time.perf_counter()
     e0.record()
     for _ in range(args.steps):
@@ -368,6 +484,7 @@ def main():
     e1.record()
     torch.cuda.synchronize()
     wall_ms = (time.perf_counter() - t0) * 1e3 / args.steps
+    clock.stop()
     ms = e0.elapsed_time(e1) / args.steps
     kinds = nsa.profile_read(reset=True)
     nsa.profile_enable(False)
@@ -401,6 +518,20 @@ def main():
                 "frac": achieved / PEAK_HBM_GBS, "traffic": traffic, "kernel": dom,
                 "bytes_per_launch": dv["bytes"] / dv["launches"], "avg_launch_ms": avg_launch_ms}
     gemm_ms = sum(v["total_ms"] for k, v in kinds.items() if k.startswith("ns_")) / args.steps
+    # Executed MFMA work of the GEMM kernels (live matrices only: idle ones
+    # are not computed) beside the nominal rate.
+    exe = {}
+    if w.dtype == "bf16":
+        for gi, j, r, c in w.matrices():
+            if not w.is_idle(gi, j):
+                for k, v in executed_mfma_flops(r, c, w.ns_steps, args.poly_form).items():
+                    exe[k] = exe.get(k, 0.0) + v
+    for k, v in exe.items():
+        if k in per_kernel and per_kernel[k]["total_ms_per_step"]:
+            rate = v / (per_kernel[k]["total_ms_per_step"] * 1e-3) / 1e12
+            per_kernel[k]["executed_tflops"] = rate
+            per_kernel[k]["executed_frac_of_peak"] = rate / PEAK_BF16_TFLOPS
+    exe_total = sum(exe.values())
 
     if args.copy_calib:
         a = torch.empty(COPY_CALIB_BYTES // 4, dtype=torch.float32, device="cuda")
@@ -421,6 +552,10 @@ def main():
         "frac_of_peak": value / peak_step,
         "ns_gemm_tflops": flops_per_step / (gemm_ms * 1e-3) / 1e12 if gemm_ms else None,
         "ns_gemm_tflops_live": live_flops_per_step / (gemm_ms * 1e-3) / 1e12 if gemm_ms else None,
+        "ns_gemm_executed_tflops": exe_total / (gemm_ms * 1e-3) / 1e12 if gemm_ms and exe_total else None,
+        "ns_gemm_executed_frac_of_peak": (exe_total / (gemm_ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS
+                                          if gemm_ms and exe_total else None),
+        "poly_form": args.poly_form,
         "idle_matrices": idle,
         "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
         "ms_per_step": ms, "wall_ms_per_step": wall_ms,
@@ -432,7 +567,7 @@ def main():
         "roofline": roof,
         "kernels": per_kernel,
         "cpu_baseline": cpu,
-        "env": environment(),
+        "env": dict(environment(), clock=clock.summary()),
     }
     print(json.dumps(out), flush=True)
 

@@ -14,8 +14,11 @@
  *                                          smaller dimension)
  *   X    = X / (||X||_F + eps)            eps = 1e-7
  *   repeat ns_steps times:                (section 6.6: one batched NS
- *     A = X X^T; B = b A + c A A;          iteration over each shape group;
- *     X = a X + B X                        (a,b,c) = (3.4445,-4.7750,2.0315))
+ *     A = X X^T; B = b A + c A A;          iteration over each shape group)
+ *     X = a X + B X
+ *   with (a,b,c) = (3.4445,-4.7750,2.0315), the standard Muon quintic: the
+ *   paper names this "legacy quintic" set (sections 6.6, 7.4) but prints
+ *   no values.
  *   O    = X, transposed back if needed
  *   p'   = p*(1 - lr*wd) - lr*scale*O      (section 6.4 step 4: update with
  *                                          weight decay; scale = 0.2*sqrt(
@@ -86,10 +89,29 @@ enum {
 #define MUON_MAX_DIM (1 << 20)
 #define MUON_DEFAULT_BATCH_CAP ((size_t)1 << 29)
 
+/* Forms of the NS polynomial step on the bf16 path (muon_options.poly_form).
+ *   MUON_POLY_SQUARE (default): with c != 0 the polynomial completed to a
+ *     square, a I + b A + c A^2 = c (A + beta I)^2 + (a - b^2/(4c)) I, beta =
+ *     b/(2c): Gram writes A + beta I, Poly c (A + beta I)^2 + (a - b^2/(4c)) I
+ *     and Update B' X, so no epilogue reads an operand tile. The diagonal of
+ *     A + beta I and of B' is rounded to bf16 after the constants are added,
+ *     which costs accuracy: measured relative Frobenius error of the update
+ *     1.0-1.6e-2 on the workload shapes, against 0.8-1.3e-2 for the direct
+ *     form (both within 2e-2).
+ *   MUON_POLY_DIRECT: the step as section 6.6 states it -- A = X X^T, B = b A
+ *     + c A A (b A added in fp32 from the A tile in the epilogue), X' = a X +
+ *     B X (a X added in fp32 from the X tile in the epilogue); A, B and X'
+ *     are each rounded once. About 7% slower on 1408 x 2048 matrices.
+ * The float32 path always computes the direct form. */
+enum { MUON_POLY_DIRECT = 0, MUON_POLY_SQUARE = 1 };
+
 /* Options. Section 6.2 of the paper makes the momentum rule, the NS step
  * count, coefficients and epsilon, and the update scale configurable
- * stages; the defaults below are the standard Muon settings of section
- * 7.4. Pass NULL for all defaults, or fill with muon_default_options(). */
+ * stages. The defaults below are standard Muon settings: section 7.4 states
+ * momentum 0.95 with Nesterov and five NS iterations; epsilon, the update
+ * scale constant and the coefficient values are not printed in the paper
+ * and follow the standard Muon definition. Pass NULL for all defaults, or
+ * fill with muon_default_options(). */
 typedef struct muon_options {
   int nesterov;           /* 1 (default): NS input is the Nesterov look-ahead u;
                              0: NS input is buf'                                  */
@@ -102,8 +124,11 @@ typedef struct muon_options {
   float rms_target;       /* default 0.2                                          */
   float eps;              /* Frobenius normalisation epsilon; default 1e-7        */
   const float* coeffs;    /* HOST array of ns_steps*3 floats (a,b,c per step), or
-                             NULL for (3.4445,-4.7750,2.0315) at every step
-                             (section 6.2: per-step coefficient sets)           */
+                             NULL for the standard Muon quintic (3.4445,
+                             -4.7750, 2.0315) at every step (section 6.2:
+                             coefficients are a configurable stage; section
+                             6.6 names the legacy quintic and an asymmetric
+                             five-step set but prints neither)              */
   size_t batch_cap_elems; /* max sum of rows*cols per fused batch; 0 => 2^29
                              (or MUON_BATCH_CAP from the environment)
                              (section 6.6: memory-safe batching). A matrix larger
@@ -126,6 +151,18 @@ typedef struct muon_options {
                              FP32 optimizer state); the update is applied to
                              the fp32 params. MUON_F32 with dtype MUON_BF16:
                              bf16 tensors iterated in fp32.                   */
+  int poly_form;          /* MUON_POLY_SQUARE (default) or MUON_POLY_DIRECT     */
+  /* Per-parameter coefficient sets (section 6.2: per-parameter coefficient
+   * sets reuse the same buffers). num_coeff_sets = 0 (default): `coeffs`
+   * applies to every matrix. K > 0: coeffs must be NULL; coeff_sets is a
+   * HOST array of K tables of ns_steps*3 floats (a,b,c per step) and
+   * coeff_set_of a HOST array with one set index in [0, K) per matrix of
+   * the call (muon_step / muon_step_views: mats[i]; muon_orthogonalize:
+   * in[i]). Matrices of one shape with different sets run in separate
+   * batches of the same workspace. */
+  int num_coeff_sets;
+  const float* coeff_sets;
+  const int* coeff_set_of;
 } muon_options;
 
 /* Fills *opts with the defaults above. */
@@ -203,6 +240,7 @@ typedef struct muon_plan_batch {
   int m_pad, n_pad;   /* padded wide shape the GEMM kernels iterate over    */
   int first;          /* offset of this batch's first matrix in `order`     */
   int count;          /* matrices in this batch                             */
+  int coeff_set;      /* coefficient set of the batch (0 without sets)      */
 } muon_plan_batch;
 
 /* Computes the plan muon_step would execute for matrices of the given

@@ -8,14 +8,21 @@
 //   Gram   : A' = sc * X X^T + beta I                 rows of X . rows of X    (K = n)
 //   Poly   : B' = c * (A' A'^T) + (a - b^2/(4c)) I    rows of A'. rows of A'   (K = m)
 //   Update : X' = sc * (B' X)                         rows of B'. columns of X (K = m)
-// with beta = b/(2c). The page writes the step as X' = a X + B X with
-// B = b A + c A A. Here the a X term moves into B' (the same product), and
-// the polynomial is completed to a square, a I + b A + c A^2 = c (A + beta
-// I)^2 + (a - b^2/(4c)) I, so neither Poly nor Update reads an operand tile
-// in its epilogue. Each changes one rounding: the diagonal of A' and of B'
-// is rounded to bf16 after the constant is added, an error of the order of
-// the rounding of A and X themselves. When c = 0 (a caller's coefficient
-// table) Gram writes A and Poly forms b A + c A A + a I with the A tile.
+// with beta = b/(2c) (the square form). The page writes the step as X' =
+// a X + B X with B = b A + c A A. The square form moves the a X term into
+// B' (the same product) and completes the polynomial to a square, a I + b A
+// + c A^2 = c (A + beta I)^2 + (a - b^2/(4c)) I, so neither Poly nor Update
+// reads an operand tile in its epilogue. That costs accuracy: the diagonal
+// of A' = A + beta I (about -1.17 against entries of A of about 1/m) and of
+// B' is rounded to bf16 after the constants are added, which loses most of
+// the bits of A's own diagonal; measured against the fp64 reference at
+// 1408 x 2048 the update's error is 1.0-1.25e-2 against 0.8-0.95e-2 for
+// the page's form. The direct form is the page's:
+//   Gram   : A  = sc * X X^T
+//   Poly   : B  = b A + c (A A^T)        (the A tile read in the epilogue)
+//   Update : X' = sc * (a X + B X)       (the X tile read in the epilogue)
+// each rounded once. When c = 0 (a caller's coefficient table) the square
+// form has Gram write A and Poly form b A + c A A + a I with the A tile.
 // A' and B' are symmetric: Gram and Poly compute only the tiles on or below
 // the diagonal and store each one twice (tile and mirror). Update stores
 // X'. sc is the first step's Frobenius scale (s^2 for Gram, s for
@@ -441,11 +448,13 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& g, int mat, int I, int
     if (WIDE && (I == J || I == J + 1)) diag_off = (I - J) * TILE;
   }
 
-  if (ROLE == kPoly && g.poly_operand) {
-    // Epilogue operand tile A into T: 128 loads of 1 KiB, 32 per wave; lane
-    // l of a load takes stored chunk l % TC8 of its row, i.e. source chunk
-    // (l % TC8) ^ eswz(row).
-    const bf16_t* E = static_cast<const bf16_t*>(g.a) + (size_t)mat * g.mat_a + (size_t)(I * TILE) * ldo;
+  if ((ROLE == kPoly && g.poly_operand) || (ROLE == kUpdate && g.update_operand)) {
+    // Epilogue operand tile into T (Poly: A, Update: X): 128 loads of 1
+    // KiB, 32 per wave; lane l of a load takes stored chunk l % TC8 of its
+    // row, i.e. source chunk (l % TC8) ^ eswz(row).
+    const bf16_t* E = (ROLE == kUpdate)
+        ? static_cast<const bf16_t*>(g.x) + (size_t)mat * g.mat_x + (size_t)(I * TILE) * ldo
+        : static_cast<const bf16_t*>(g.a) + (size_t)mat * g.mat_a + (size_t)(I * TILE) * ldo;
     constexpr int RPI = 1024 / (QR * 2);   // tile rows per load
 #pragma unroll 8
     for (int q = 0; q < 32; ++q) {
@@ -465,8 +474,9 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& g, int mat, int I, int
   // every read after the previous write).
   //   Gram:   A' = sc * acc + d I          (d = diag_add: b/(2c), or 0)
   //   Poly:   B' = c acc + d I             (acc = A'A', d = a - b^2/(4c))
-  //      or   B' = b A + c acc + a I       (operand tile A, when c = 0)
+  //      or   B' = b A + c acc + d I       (operand tile A; d = a or 0)
   //   Update: X' = sc * acc                (acc = B' X)
+  //      or   X' = sc * (a X + acc)        (operand tile X; acc = B X)
   // d is added by the DG instances, on diagonal tiles only.
   // A wave's block holds diagonal elements only if rb0 + diag_off == cb0;
   // then they sit in acc[b][b], element 4*(l/8) + l%4 (l = lane % 32) of
@@ -504,8 +514,13 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& g, int mat, int I, int
         if (OP) {
           const float x[4] = {bf16_to_f32(w[a][q].x & 0xffffu), bf16_to_f32(w[a][q].x >> 16),
                               bf16_to_f32(w[a][q].y & 0xffffu), bf16_to_f32(w[a][q].y >> 16)};
+          if (ROLE == kPoly) {
 #pragma unroll
-          for (int e = 0; e < 4; ++e) v[e] = fmaf(g.cb, x[e], g.cc * v[e]);
+            for (int e = 0; e < 4; ++e) v[e] = fmaf(g.cb, x[e], g.cc * v[e]);
+          } else {
+#pragma unroll
+            for (int e = 0; e < 4; ++e) v[e] = SC ? sc * fmaf(g.ca, x[e], v[e]) : fmaf(g.ca, x[e], v[e]);
+          }
         } else if (ROLE == kPoly) {
 #pragma unroll
           for (int e = 0; e < 4; ++e) v[e] *= g.cc;
@@ -540,6 +555,8 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& g, int mat, int I, int
     } else {
       if (dgon) form(T1{}, F0{}, F0{}); else form(F0{}, F0{}, F0{});
     }
+  } else if (g.update_operand) {
+    if (g.scales) form(F0{}, T1{}, T1{}); else form(F0{}, F0{}, T1{});
   } else {
     if (g.scales) form(F0{}, T1{}, F0{}); else form(F0{}, F0{}, F0{});
   }

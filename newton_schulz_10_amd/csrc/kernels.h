@@ -95,10 +95,15 @@ struct ApplyArgs {
 // element strides per matrix given below. Symmetric roles compute only the
 // tiles on one side of the diagonal and mirror them.
 //   fp32 kernels: Poly writes B = b*A + c*(A A), Update X' = sc*(a*X + B X).
-//   bf16 kernels: Poly writes B' = a*I + b*A + c*(A A), Update X' = sc*(B' X)
-//                 (the same product, with a*X moved into B'); with c != 0,
-//                 Gram writes A' = A + (b/2c) I and Poly B' = c A'A' +
-//                 (a - b^2/4c) I, the same polynomial completed to a square.
+//   bf16 kernels, by muon_options.poly_form:
+//     MUON_POLY_SQUARE: with c != 0, Gram writes A' = A + (b/2c) I, Poly
+//                 B' = c A'A' + (a - b^2/4c) I = a I + b A + c A A and
+//                 Update X' = sc (B' X), so no epilogue reads an operand
+//                 tile; with c = 0, Poly writes B' = a I + b A + c A A with
+//                 the A tile and Update X' = sc (B' X).
+//     MUON_POLY_DIRECT: as the fp32 kernels (A, then b A + c A A with the A
+//                 tile, then sc (a X + B X) with the X tile), each rounded
+//                 once to bf16.
 enum GemmRole {
   kGram = 0,    // A   = sc * X X^T                (sc = s_i^2 or 1)
   kPoly = 1,    // B   (A symmetric)
@@ -118,10 +123,13 @@ struct GemmArgs {
   const float* scales;  // per-matrix s (first iteration) or nullptr
   float ca, cb, cc;     // quintic coefficients of this step
   // bf16 kernels only: the value added on the global diagonal by Gram (A'
-  // = A + diag_add I) and Poly, and whether Poly reads the A tile in its
-  // epilogue (b A + c A A + a I) or not (c A'A' + diag_add I).
+  // = A + diag_add I) and Poly, whether Poly reads the A tile in its
+  // epilogue (b A + c A A + diag_add I) or not (c A'A' + diag_add I), and
+  // whether Update reads the X tile in its epilogue (sc (a X + B X)) or
+  // not (sc B' X).
   float diag_add;
   int poly_operand;
+  int update_operand;
   // bf16 Update only: when ptab is set, the tile is not stored as X' but
   // applied: p' = alpha*p - gamma[tr]*O (apply_mode 0) or out = O (1), O
   // being X' rounded to bf16, in the matrix's original orientation.

@@ -179,7 +179,9 @@ int run(const std::vector<MatRef>& mats, float lr, float beta, int ns_steps, muo
   const muon_dtype ns = ns_type(o, dtype);
   Plan plan;
   std::string err;
-  int rc = build_plan(rows.data(), cols.data(), num, ns, o.batch_cap_elems, fit_units(o), plan, err);
+  const int* set_of = o.num_coeff_sets > 0 ? o.coeff_set_of : nullptr;
+  int rc = build_plan(rows.data(), cols.data(), num, ns, o.batch_cap_elems, fit_units(o), plan, err, set_of,
+                      o.num_coeff_sets);
   if (rc) return fail(rc, err);
 
   if (const char* f = std::getenv("MUON_TEST_FAIL_ALLOC"))
@@ -274,6 +276,9 @@ int run(const std::vector<MatRef>& mats, float lr, float beta, int ns_steps, muo
     }
 
     // 3. NS iterations; the Frobenius scale is folded into the first step.
+    // The batch's coefficient table: its set's (per-parameter sets), the
+    // call's, or the standard quintic at every step.
+    const float* tab = o.num_coeff_sets > 0 ? o.coeff_sets + (size_t)B.set * (size_t)ns_steps * 3 : o.coeffs;
     void* X = x0;
     void* Xn = x1;
     for (int k = 0; k < ns_steps && status == MUON_OK; ++k) {
@@ -281,18 +286,24 @@ int run(const std::vector<MatRef>& mats, float lr, float beta, int ns_steps, muo
       GemmArgs g{};
       g.mat_x = L.mat_x; g.mat_a = L.mat_a; g.count = B.count;
       g.m = B.m; g.n = B.n; g.m_pad = B.m_pad; g.n_pad = B.n_pad;
-      g.ca = o.coeffs ? o.coeffs[3 * k + 0] : 3.4445f;
-      g.cb = o.coeffs ? o.coeffs[3 * k + 1] : -4.7750f;
-      g.cc = o.coeffs ? o.coeffs[3 * k + 2] : 2.0315f;
-      // bf16: with c != 0 the polynomial is completed to a square,
+      g.ca = tab ? tab[3 * k + 0] : 3.4445f;
+      g.cb = tab ? tab[3 * k + 1] : -4.7750f;
+      g.cc = tab ? tab[3 * k + 2] : 2.0315f;
+      // bf16, MUON_POLY_DIRECT: Gram writes A, Poly b A + c A A (A tile in
+      // its epilogue), Update a X + B X (X tile in its epilogue).
+      // MUON_POLY_SQUARE with c != 0: the polynomial is completed to a square,
       //   a I + b A + c A^2 = c (A + beta I)^2 + (a - b^2/(4c)) I,
       //   beta = b / (2c),
-      // so Gram writes A' = A + beta I and Poly needs no A tile. The step's
-      // arithmetic is in double, rounded once to float.
-      const bool shifted = bf16 && g.cc != 0.0f;
+      // so Gram writes A' = A + beta I, Poly c A'A' + (a - b^2/(4c)) I and
+      // Update B' X, with no operand tile; with c = 0 Poly forms a I + b A
+      // + c A A with the A tile. The step's arithmetic is in double,
+      // rounded once to float.
+      const bool square = bf16 && o.poly_form == MUON_POLY_SQUARE;
+      const bool shifted = square && g.cc != 0.0f;
       const double beta_sq = shifted ? (double)g.cb / (2.0 * (double)g.cc) : 0.0;
       const float gram_diag = (float)beta_sq;
-      const float poly_diag = shifted ? (float)((double)g.ca - (double)g.cb * (double)g.cb / (4.0 * (double)g.cc)) : g.ca;
+      const float poly_diag = shifted ? (float)((double)g.ca - (double)g.cb * (double)g.cb / (4.0 * (double)g.cc))
+                                      : (square ? g.ca : 0.0f);
       const GemmRole roles[3] = {kGram, kPoly, kUpdate};
       const char* names[3] = {"ns_gram", "ns_poly", "ns_update"};
       for (int r = 0; r < 3; ++r) {
@@ -309,6 +320,7 @@ int run(const std::vector<MatRef>& mats, float lr, float beta, int ns_steps, muo
         // zeroed by the compact kernel.
         g.sched = (skip_zero && r == 0) ? sched : nullptr;
         g.poly_operand = shifted ? 0 : 1;
+        g.update_operand = (bf16 && !square) ? 1 : 0;
         const bool apply_here = fused_apply && r == 2 && k + 1 == ns_steps;
         g.ptab = apply_here ? ptab : nullptr;
         g.alpha = apply_alpha;
@@ -541,12 +553,17 @@ int muon_plan_query(const int* rows, const int* cols, int num, muon_dtype dtype,
     if (o.compute_units < -1) return fail(MUON_ERR_INVALID_ARGUMENT, "options.compute_units must be >= -1");
     if (o.ns_dtype != -1 && o.ns_dtype != MUON_F32 && o.ns_dtype != MUON_BF16)
       return fail(MUON_ERR_INVALID_ARGUMENT, "options.ns_dtype must be -1, MUON_F32 or MUON_BF16");
-    int rc = build_plan(rows, cols, num, ns_type(o, dtype), o.batch_cap_elems, fit_units(o), plan, err);
+    if (o.num_coeff_sets < 0) return fail(MUON_ERR_INVALID_ARGUMENT, "options.num_coeff_sets must be >= 0");
+    if (o.num_coeff_sets > 0 && !o.coeff_set_of)
+      return fail(MUON_ERR_INVALID_ARGUMENT, "options.coeff_set_of is required when num_coeff_sets > 0");
+    const int* set_of = o.num_coeff_sets > 0 ? o.coeff_set_of : nullptr;
+    int rc = build_plan(rows, cols, num, ns_type(o, dtype), o.batch_cap_elems, fit_units(o), plan, err, set_of,
+                        o.num_coeff_sets);
     if (rc) return fail(rc, err);
     if (cap > 0 && !batches) return fail(MUON_ERR_INVALID_ARGUMENT, "batches is NULL with cap > 0");
     for (int i = 0; i < cap && i < (int)plan.batches.size(); ++i) {
       const Batch& b = plan.batches[i];
-      batches[i] = muon_plan_batch{b.group, b.m, b.n, b.m_pad, b.n_pad, b.first, b.count};
+      batches[i] = muon_plan_batch{b.group, b.m, b.n, b.m_pad, b.n_pad, b.first, b.count, b.set};
     }
     if (num_batches) *num_batches = (int)plan.batches.size();
     if (order) std::copy(plan.order.begin(), plan.order.end(), order);

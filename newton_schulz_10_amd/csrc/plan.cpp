@@ -80,42 +80,71 @@ static double ns_batch_cost(long long c, int m_pad, int n_pad, int cus) {
 }
 
 int build_plan(const int* rows, const int* cols, int num, muon_dtype dtype, size_t cap, int cus,
-               Plan& out, std::string& err) {
+               Plan& out, std::string& err, const int* set_of, int num_sets, size_t max_ws) {
   out = Plan();
   if (num < 0) { err = "num < 0"; return MUON_ERR_INVALID_ARGUMENT; }
   if (num > 0 && (!rows || !cols)) { err = "rows/cols array is NULL"; return MUON_ERR_INVALID_ARGUMENT; }
   if (dtype != MUON_F32 && dtype != MUON_BF16) { err = "unknown dtype"; return MUON_ERR_INVALID_ARGUMENT; }
   if (cap == 0) cap = MUON_DEFAULT_BATCH_CAP;
+  if (set_of && num_sets < 1) { err = "coefficient sets given with num_sets < 1"; return MUON_ERR_INVALID_ARGUMENT; }
   out.transposed.resize(num);
-  // key = (min, max); groups keep first-appearance order of their matrices.
-  std::map<std::pair<int, int>, std::vector<int>> groups;
+  // key = (min, max, set); groups keep first-appearance order of their
+  // matrices.
+  std::map<std::tuple<int, int, int>, std::vector<int>> groups;
   for (int i = 0; i < num; ++i) {
     int rc = check_shape(rows[i], cols[i], err, i);
     if (rc) return rc;
+    const int set = set_of ? set_of[i] : 0;
+    if (set < 0 || (set_of && set >= num_sets)) {
+      std::ostringstream s;
+      s << "matrix " << i << ": coefficient set " << set << " outside [0, " << num_sets << ")";
+      err = s.str();
+      return MUON_ERR_INVALID_ARGUMENT;
+    }
     out.transposed[i] = rows[i] > cols[i] ? 1 : 0;
-    groups[{std::min(rows[i], cols[i]), std::max(rows[i], cols[i])}].push_back(i);
+    groups[{std::min(rows[i], cols[i]), std::max(rows[i], cols[i]), set}].push_back(i);
   }
   // Descending element count (large matrices first); ties: larger long
-  // side first, then larger short side.
-  std::vector<std::pair<std::pair<int, int>, std::vector<int>>> g(groups.begin(), groups.end());
+  // side first, then larger short side, then lower set index.
+  std::vector<std::pair<std::tuple<int, int, int>, std::vector<int>>> g(groups.begin(), groups.end());
   std::stable_sort(g.begin(), g.end(), [](const auto& x, const auto& y) {
-    long long ex = (long long)x.first.first * x.first.second;
-    long long ey = (long long)y.first.first * y.first.second;
+    const int xm = std::get<0>(x.first), xn = std::get<1>(x.first), ym = std::get<0>(y.first),
+              yn = std::get<1>(y.first);
+    long long ex = (long long)xm * xn;
+    long long ey = (long long)ym * yn;
     if (ex != ey) return ex > ey;
-    if (x.first.second != y.first.second) return x.first.second > y.first.second;
-    return x.first.first > y.first.first;
+    if (xn != yn) return xn > yn;
+    if (xm != ym) return xm > ym;
+    return std::get<2>(x.first) < std::get<2>(y.first);
   });
   const int pgm = pad_granularity_m(dtype), pgn = pad_granularity_n(dtype);
   size_t ws = 0;
   for (size_t gi = 0; gi < g.size(); ++gi) {
-    const int m = g[gi].first.first, n = g[gi].first.second;
+    const int m = std::get<0>(g[gi].first), n = std::get<1>(g[gi].first), set = std::get<2>(g[gi].first);
     const std::vector<int>& idx = g[gi].second;
     const int cnt = (int)idx.size();
     const size_t per_mat = (size_t)m * (size_t)n;
     size_t per_batch = std::max<size_t>(1, cap / per_mat);
-    int nb = (int)((cnt + per_batch - 1) / per_batch);
     const int m_pad = (int)round_up(m, pgm), n_pad = (int)round_up(n, pgn);
-    if (dtype == MUON_BF16 && cus > 0 && cnt > 1) {
+    if (max_ws > 0) {
+      // Workspace bound: the largest count whose batch layout fits.
+      if (batch_layout(1, m_pad, n_pad, dtype).total > max_ws) {
+        std::ostringstream s;
+        s << "matrix " << idx[0] << " (" << rows[idx[0]] << " x " << cols[idx[0]] << ") needs "
+          << batch_layout(1, m_pad, n_pad, dtype).total << " bytes of workspace, more than the "
+          << max_ws << " available";
+        err = s.str();
+        return MUON_ERR_INVALID_ARGUMENT;
+      }
+      size_t lo = 1, hi = std::min<size_t>(per_batch, (size_t)cnt);
+      while (lo < hi) {
+        const size_t mid = (lo + hi + 1) / 2;
+        if (batch_layout((int)mid, m_pad, n_pad, dtype).total <= max_ws) lo = mid; else hi = mid - 1;
+      }
+      per_batch = lo;
+    }
+    int nb = (int)((cnt + per_batch - 1) / per_batch);
+    if (dtype == MUON_BF16 && cus > 0 && cnt > 1 && max_ws == 0) {
       // Up to four more batches than needed, if their tiles fill the
       // compute units' rounds better (balanced sizes, as below).
       double best = 0.0;
@@ -130,7 +159,7 @@ int build_plan(const int* rows, const int* cols, int num, muon_dtype dtype, size
     int start = 0;
     for (int b = 0; b < nb; ++b) {
       int c = cnt / nb + (b < cnt % nb ? 1 : 0);  // balanced sizes
-      Batch B{(int)gi, m, n, m_pad, n_pad, (int)out.order.size(), c};
+      Batch B{(int)gi, m, n, m_pad, n_pad, (int)out.order.size(), c, set};
       for (int k = 0; k < c; ++k) out.order.push_back(idx[start + k]);
       start += c;
       out.batches.push_back(B);
@@ -152,6 +181,10 @@ void default_options(muon_options& o) {
   o.batch_cap_elems = MUON_DEFAULT_BATCH_CAP;
   o.compute_units = 0;
   o.ns_dtype = -1;
+  o.poly_form = MUON_POLY_SQUARE;
+  o.num_coeff_sets = 0;
+  o.coeff_sets = nullptr;
+  o.coeff_set_of = nullptr;
 }
 
 int check_options(const muon_options& o, int ns_steps, std::string& err) {
@@ -169,6 +202,23 @@ int check_options(const muon_options& o, int ns_steps, std::string& err) {
     for (int i = 0; i < 3 * ns_steps; ++i)
       if (!std::isfinite(o.coeffs[i])) {
         std::ostringstream s; s << "options.coeffs[" << i << "] is not finite"; err = s.str();
+        return MUON_ERR_INVALID_ARGUMENT;
+      }
+  }
+  if (o.poly_form != MUON_POLY_DIRECT && o.poly_form != MUON_POLY_SQUARE) {
+    err = "options.poly_form must be MUON_POLY_DIRECT or MUON_POLY_SQUARE"; return MUON_ERR_INVALID_ARGUMENT;
+  }
+  if (o.num_coeff_sets < 0) { err = "options.num_coeff_sets must be >= 0"; return MUON_ERR_INVALID_ARGUMENT; }
+  if (o.num_coeff_sets > 0) {
+    if (o.coeffs) { err = "options.coeffs must be NULL when num_coeff_sets > 0"; return MUON_ERR_INVALID_ARGUMENT; }
+    if (!o.coeff_sets || !o.coeff_set_of) {
+      err = "options.coeff_sets and options.coeff_set_of are required when num_coeff_sets > 0";
+      return MUON_ERR_INVALID_ARGUMENT;
+    }
+    const long long total = 3LL * ns_steps * o.num_coeff_sets;
+    for (long long i = 0; i < total; ++i)
+      if (!std::isfinite(o.coeff_sets[i])) {
+        std::ostringstream s; s << "options.coeff_sets[" << i << "] is not finite"; err = s.str();
         return MUON_ERR_INVALID_ARGUMENT;
       }
   }

@@ -32,6 +32,7 @@ struct Batch {
   int m_pad, n_pad;
   int first;   // offset into Plan::order
   int count;
+  int set;     // coefficient set of every matrix of the batch (0 without sets)
 };
 
 struct Plan {
@@ -60,13 +61,17 @@ size_t dtype_size(muon_dtype dtype);
 
 Layout batch_layout(int count, int m_pad, int n_pad, muon_dtype dtype);
 
-// Groups matrices by {min, max}, orders groups by descending rows*cols,
-// splits each group into balanced batches of at most `cap` elements. With
-// cus > 0 (bf16), the number of batches is the one, among the fewest and a
-// few more, whose GEMM tiles best fill whole rounds of `cus` compute units.
-// Returns MUON_OK or MUON_ERR_INVALID_ARGUMENT with `err` set.
+// Groups matrices by {min, max} and, when `set_of` is given, by their
+// coefficient set set_of[i] in [0, num_sets); orders groups by descending
+// rows*cols (then set); splits each group into balanced batches of at most
+// `cap` elements and, when max_ws > 0, of at most max_ws workspace bytes.
+// With cus > 0 (bf16), the number of batches is the one, among the fewest
+// and a few more, whose GEMM tiles best fill whole rounds of `cus` compute
+// units. Returns MUON_OK, or MUON_ERR_INVALID_ARGUMENT with `err` set (a
+// bad shape or set index, or one matrix whose workspace exceeds max_ws).
 int build_plan(const int* rows, const int* cols, int num, muon_dtype dtype, size_t cap, int cus,
-               Plan& out, std::string& err);
+               Plan& out, std::string& err, const int* set_of = nullptr, int num_sets = 0,
+               size_t max_ws = 0);
 
 // Option defaults and validation.
 void default_options(muon_options& o);

@@ -22,9 +22,13 @@ relies on:
   * section 6.6: tall matrices are transposed first so the Gram product
     is taken on the smaller dimension; the original quintic is one of two
     coefficient sets;
-  * section 7.4: momentum 0.95 with Nesterov, 5 NS iterations with the
-    fixed quintic coefficients (3.4445, -4.7750, 2.0315), an update scale
-    that matches RMS, and FP32 optimizer state.
+  * section 7.4: momentum 0.95 with Nesterov, 5 NS iterations with fixed
+    NS coefficients, an update scale that matches RMS, and FP32 optimizer
+    state.
+
+The coefficient values (3.4445, -4.7750, 2.0315) are not printed anywhere
+on the page: sections 6.6 and 7.4 name the "legacy quintic" set, and the
+values are those of the standard Muon quintic.
 
 Every function works on float64 numpy arrays, one matrix at a time, with
 numpy's matmul as the only library step. No blocking, fusion or reordering
@@ -38,9 +42,9 @@ from typing import Iterable, List, Optional, Sequence, Tuple, Union
 
 import numpy as np
 
-# Quintic coefficients (a, b, c) of p(s) = a s + b s^3 + c s^5: the original
-# Muon set, which section 6.6 lists as one of two selectable sets and which
-# section 7.4's torch.optim.Muon baseline uses as its fixed coefficients.
+# Quintic coefficients (a, b, c) of p(s) = a s + b s^3 + c s^5: the standard
+# Muon set. Section 6.6 lists the legacy quintic as one of two selectable
+# sets, without its values; these are the standard definition's.
 QUINTIC_COEFFS: Tuple[float, float, float] = (3.4445, -4.7750, 2.0315)
 
 Coeffs = Union[Tuple[float, float, float], Sequence[Tuple[float, float, float]]]

@@ -26,3 +26,14 @@ def pytest_collection_modifyitems(config, items):
     for item in items:
         if "gpu" in item.keywords:
             item.add_marker(skip)
+
+
+def pytest_terminal_summary(terminalreporter):
+    # The parity numbers of the GPU tests (every comparison against the
+    # oracle), printed even under -q so that a run's log carries them.
+    mod = sys.modules.get("gpu_helpers")
+    if mod is None or not getattr(mod, "RECORDS", None):
+        return
+    terminalreporter.section("parity against the fp64 oracle (err / raw / worst 256x256 tile)")
+    for line in mod.summary_lines(mod.RECORDS):
+        terminalreporter.write_line(line)

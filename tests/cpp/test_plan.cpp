@@ -115,6 +115,61 @@ int main() {
     o.ns_dtype = MUON_BF16;
     CHECK(check_options(o, 5, err) == MUON_OK);
   }
+  // Coefficient sets: a shape group splits by set, sets in ascending order
+  // after the element-count order; a bad index is an error.
+  {
+    std::vector<int> r = {256, 384, 256, 100, 384}, c = {384, 256, 384, 60, 256}, set = {1, 0, 0, 1, 1};
+    Plan p;
+    CHECK(build_plan(r.data(), c.data(), 5, MUON_BF16, 0, 0, p, err, set.data(), 2) == MUON_OK);
+    CHECK(p.batches.size() == 3);
+    CHECK(p.batches[0].m == 256 && p.batches[0].n == 384 && p.batches[0].set == 0 && p.batches[0].count == 2);
+    CHECK(p.batches[1].m == 256 && p.batches[1].n == 384 && p.batches[1].set == 1 && p.batches[1].count == 2);
+    CHECK(p.batches[2].m == 60 && p.batches[2].set == 1 && p.batches[2].count == 1);
+    CHECK(p.order[0] == 1 && p.order[1] == 2 && p.order[2] == 0 && p.order[3] == 4 && p.order[4] == 3);
+    Plan q;
+    CHECK(build_plan(r.data(), c.data(), 5, MUON_BF16, 0, 0, q, err) == MUON_OK);
+    CHECK(q.batches.size() == 2 && q.batches[0].count == 4 && q.batches[0].set == 0);
+    set[3] = 2;
+    CHECK(build_plan(r.data(), c.data(), 5, MUON_BF16, 0, 0, p, err, set.data(), 2) == MUON_ERR_INVALID_ARGUMENT);
+    CHECK(err.find("matrix 3") != std::string::npos);
+    set[3] = -1;
+    CHECK(build_plan(r.data(), c.data(), 5, MUON_BF16, 0, 0, p, err, set.data(), 2) == MUON_ERR_INVALID_ARGUMENT);
+    CHECK(build_plan(r.data(), c.data(), 5, MUON_BF16, 0, 0, p, err, set.data(), 0) == MUON_ERR_INVALID_ARGUMENT);
+    muon_options o;
+    default_options(o);
+    CHECK(o.poly_form == MUON_POLY_SQUARE && o.num_coeff_sets == 0);
+    o.poly_form = 2;
+    CHECK(check_options(o, 5, err) == MUON_ERR_INVALID_ARGUMENT);
+    default_options(o);
+    o.num_coeff_sets = 1;
+    CHECK(check_options(o, 5, err) == MUON_ERR_INVALID_ARGUMENT);   // tables missing
+    float tab[15] = {3, -3, 1, 3, -3, 1, 3, -3, 1, 3, -3, 1, 3, -3, 1};
+    int of[1] = {0};
+    o.coeff_sets = tab;
+    o.coeff_set_of = of;
+    CHECK(check_options(o, 5, err) == MUON_OK);
+    o.coeffs = tab;
+    CHECK(check_options(o, 5, err) == MUON_ERR_INVALID_ARGUMENT);   // coeffs and sets together
+    o.coeffs = nullptr;
+    tab[7] = 1.0f / 0.0f;
+    CHECK(check_options(o, 5, err) == MUON_ERR_INVALID_ARGUMENT);
+  }
+  // Workspace bound: batches hold as many matrices as fit in max_ws bytes;
+  // a matrix that alone needs more is an error naming it.
+  {
+    std::vector<int> r(40, 1408), c(40, 2048);
+    const size_t one = batch_layout(1, 1408, 2048, MUON_BF16).total;
+    const size_t lim = batch_layout(7, 1408, 2048, MUON_BF16).total;
+    Plan p;
+    CHECK(build_plan(r.data(), c.data(), 40, MUON_BF16, 0, 0, p, err, nullptr, 0, lim) == MUON_OK);
+    CHECK(p.batches.size() == 6);   // 40 = 7+7+7+7+6+6 in balanced batches of at most 7
+    for (auto& b : p.batches) CHECK(b.count <= 7 && b.count >= 6);
+    CHECK(p.workspace_bytes <= lim);
+    CHECK(build_plan(r.data(), c.data(), 40, MUON_BF16, 0, 256, p, err, nullptr, 0, lim) == MUON_OK);
+    CHECK(p.workspace_bytes <= lim);   // no refit beyond the bound
+    CHECK(build_plan(r.data(), c.data(), 40, MUON_BF16, 0, 0, p, err, nullptr, 0, one - 1) == MUON_ERR_INVALID_ARGUMENT);
+    CHECK(err.find("matrix 0 (1408 x 2048)") != std::string::npos);
+  }
   // Strided views of one parameter (bytes; a 4 x 64-byte parameter at 0x1000).
   {
     const auto at = [](unsigned long long a) { return reinterpret_cast<const void*>(uintptr_t(a)); };

@@ -326,3 +326,68 @@ def test_view_overlap_check_against_brute_force(lib, monkeypatch):
                     expect_bad = True
         rc, msg = _call_views(lib, views)
         assert rc == (1 if expect_bad else 4), (trial, views, msg)
+
+
+# ---- binding: tensor forms and the checks the C interface cannot make ------
+
+def test_matrix_layout_tensor_forms():
+    # HyperParallel-FSDP section 6.6 (Figure 10(a)): [A, B], [A, 1, B] and
+    # [N, A, B] share the (A, B) group; section 6.3: [N, A, B] is N matrices.
+    from newton_schulz_10_amd import matrix_layout
+    assert matrix_layout((6, 10)) == [(0, 6, 10)]
+    assert matrix_layout((6, 1, 10)) == [(0, 6, 10)]
+    assert matrix_layout((3, 6, 10)) == [(0, 6, 10), (60, 6, 10), (120, 6, 10)]
+    assert matrix_layout((1, 6, 10)) == [(0, 6, 10)]
+    assert matrix_layout((1, 1, 10)) == [(0, 1, 10)]
+    with pytest.raises(ValueError):
+        matrix_layout((2, 3, 4, 5))
+    with pytest.raises(ValueError):
+        matrix_layout((7,))
+
+
+def test_plan_groups_a1b_with_ab(lib):
+    # A (6, 1, 10) tensor is one 6 x 10 matrix: it joins the (6, 10) group
+    # with a [6, 10] matrix and the two matrices of a [2, 6, 10] bank, and a
+    # [10, 6] matrix transposed.
+    import torch
+    import newton_schulz_10_amd as nsa
+    shapes = [(r, c) for t in ((6, 10), (6, 1, 10), (2, 6, 10), (10, 6)) for _, r, c in nsa.matrix_layout(t)]
+    assert shapes == [(6, 10), (6, 10), (6, 10), (6, 10), (10, 6)]
+    plan = nsa.plan_query(shapes, torch.bfloat16)
+    assert [(b["m"], b["n"], b["count"]) for b in plan["batches"]] == [(6, 10, 5)]
+
+
+def test_binding_rejects_wrong_dtypes_and_host_tensors(lib):
+    # The C interface sees only pointers; the binding must refuse tensors
+    # whose element type or device the kernels would misread (a bf16
+    # momentum would be written 4 bytes per element into 2-byte storage, a
+    # host pointer would fault the GPU). Every rejection happens before any
+    # call into the library, so no GPU is needed.
+    import torch
+    import newton_schulz_10_amd as nsa
+    bf, f32 = torch.bfloat16, torch.float32
+    p, g, m = torch.zeros(8, 16, dtype=bf), torch.zeros(8, 16, dtype=bf), torch.zeros(8, 16, dtype=f32)
+    with pytest.raises(TypeError, match="momentum"):
+        nsa.muon_step([(p, g, torch.zeros(8, 16, dtype=bf))], 0.02)
+    with pytest.raises(TypeError, match="grad"):
+        nsa.muon_step([(p, torch.zeros(8, 16, dtype=f32), m)], 0.02)
+    with pytest.raises(TypeError):
+        nsa.muon_step([(torch.zeros(8, 16, dtype=torch.float16), g, m)], 0.02)
+    with pytest.raises(ValueError, match="expected the current GPU"):
+        nsa.muon_step([(p, g, m)], 0.02)
+    with pytest.raises(TypeError, match="momentum"):
+        nsa.muon_group_step([p], [g], [torch.zeros(8, 16, dtype=bf)], 0.02)
+    with pytest.raises(TypeError, match="grads"):
+        nsa.muon_group_step([p], [torch.zeros(8, 16, dtype=f32)], [m], 0.02)
+    with pytest.raises(ValueError, match="expected the current GPU"):
+        nsa.muon_group_step([p], [g], [m], 0.02)
+    with pytest.raises(TypeError, match="momentum"):
+        nsa.muon_step_views([(p, g, torch.zeros(8, 16, dtype=bf))], 0.02)
+    with pytest.raises(TypeError, match="grad"):
+        nsa.muon_step_views([(p, torch.zeros(8, 16, dtype=f32), m)], 0.02)
+    with pytest.raises(ValueError, match="expected the current GPU"):
+        nsa.muon_step_views([(p, g, m)], 0.02)
+    with pytest.raises(TypeError, match="outputs"):
+        nsa.muon_orthogonalize([p], [torch.zeros(8, 16, dtype=f32)])
+    with pytest.raises(ValueError, match="expected the current GPU"):
+        nsa.muon_orthogonalize([p], [torch.zeros(8, 16, dtype=bf)])

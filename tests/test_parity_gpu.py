@@ -7,8 +7,8 @@ import pytest
 
 import oracle
 import workloads
-from gpu_helpers import (BF16_TOL, F32_TOL, MOM_TOL, check_update, from_device, oracle_case, rel_fro,
-                         to_device, upload_case)
+from gpu_helpers import (BF16_TOL, F32_TOL, MOM_TOL, check_momentum, check_output, check_update, from_device,
+                         oracle_case, rel_fro, to_device, upload_case)
 
 pytestmark = pytest.mark.gpu
 
@@ -38,8 +38,8 @@ def assert_parity(case, dtype, p1, m1, ref, tol):
     worst = 0.0
     for i, (c, (rp, rb, ro)) in enumerate(zip(case, ref)):
         p0 = c["params"].as_f64()
-        e = check_update(p0, p1[i], rp, dtype, tol)
-        em = rel_fro(m1[i], rb.astype(np.float32))
+        e = check_update(p0, p1[i], rp, dtype, tol, label=f"#{i}")
+        em = check_momentum(m1[i], rb, label=f"#{i}")
         worst = max(worst, e)
         assert e <= tol, (i, p0.shape, e)
         assert em <= MOM_TOL, (i, p0.shape, em)
@@ -68,7 +68,7 @@ def test_tiny_fp32_closed_form_3x5(nsa):
     nsa.muon_orthogonalize([x], [out], 5)
     torch.cuda.synchronize()
     ref = oracle.newton_schulz(g.astype(np.float64))
-    assert rel_fro(from_device(out), ref) <= F32_TOL
+    assert check_output(from_device(out), ref, "f32", F32_TOL, label="3x5") <= F32_TOL
 
 
 # ---- small and ragged shapes, several tiles -------------------------------
@@ -193,7 +193,7 @@ def test_orthogonalize_entry(nsa):
         torch.cuda.synchronize()
         for k, s in enumerate(st):
             ref = oracle.newton_schulz(s.as_f64())
-            assert rel_fro(from_device(outs[k]), ref) <= tol
+            assert check_output(from_device(outs[k]), ref, dtype, tol, label=f"#{k}") <= tol
         assert np.array_equal(from_device(ins[2]), from_device(outs[2]))
 
 
@@ -244,7 +244,7 @@ def test_repeat_calls_bitwise_with_claimed_tiles(nsa):
     nsa.muon_step(list(zip(P, G, M)), 0.02, 0.95, 5)
     torch.cuda.synchronize()
     for c, i, (rp, _, _) in zip(sub, (0, 30), ref):
-        e = check_update(c["params"].as_f64(), from_device(P[i]), rp, "bf16", BF16_TOL)
+        e = check_update(c["params"].as_f64(), from_device(P[i]), rp, "bf16", BF16_TOL, label=f"#{i}")
         assert e <= BF16_TOL, (i, e)
 
 
@@ -395,3 +395,62 @@ def test_checkpoint_resume_bitwise(nsa):
         nsa.muon_step(list(zip(P2, G, M2)), 0.02, 0.95, 5)
     torch.cuda.synchronize()
     assert all(torch.equal(a, b) for a, b in zip(P + M, P2 + M2))
+
+
+# ---- the two polynomial forms; per-parameter coefficient sets; eps, rms ----
+
+@pytest.mark.parametrize("form", ["direct", "square"])
+def test_poly_forms_ragged(nsa, form):
+    # Both bf16 forms of the NS step against the oracle over the ragged
+    # shapes (the square form, the default, completes the polynomial to a
+    # square so that no epilogue reads an operand tile; the direct form is
+    # the page's, with the operand tiles read in the epilogues).
+    case = workloads.random_case(1, RAGGED, "bf16", params_init="zero")
+    p1, m1 = run_case(nsa, case, "bf16", poly_form=form)
+    ref = oracle_case(case, 0.02, 0.95, 5)
+    worst = assert_parity(case, "bf16", p1, m1, ref, BF16_TOL)
+    _print(form, "form ragged worst rel err", worst)
+
+
+def test_per_parameter_coefficient_sets(nsa):
+    # HyperParallel-FSDP section 6.2: per-parameter coefficient sets. Three
+    # sets over matrices of two shapes, with same-shaped matrices on
+    # different sets; every matrix against the oracle with its own table,
+    # and the mixed call bitwise equal to one call per set.
+    import torch
+    quintic = [(3.4445, -4.775, 2.0315)] * 5
+    other = [(3.0, -3.2, 1.2), (3.4445, -4.775, 2.0315), (2.9, -3.0, 1.1), (3.4, -4.7, 2.0), (1.875, -1.25, 0.375)]
+    cubic = [(1.5, -0.5, 0.0)] * 5
+    sets = [quintic, other, cubic]
+    shapes = [(256, 384), (384, 256), (256, 384), (200, 330), (256, 384), (330, 200)]
+    set_of = [0, 1, 2, 1, 1, 2]
+    for dtype, tol in (("bf16", BF16_TOL), ("f32", F32_TOL)):
+        case = workloads.random_case(30, shapes, dtype, params_init="zero")
+        P, G, M = upload_case(case, dtype)
+        nsa.muon_step(list(zip(P, G, M)), 0.02, 0.95, 5, coeff_sets=sets, coeff_set_of=set_of)
+        P2, G2, M2 = upload_case(case, dtype)
+        for k in range(3):
+            idx = [i for i, s in enumerate(set_of) if s == k]
+            nsa.muon_step([(P2[i], G2[i], M2[i]) for i in idx], 0.02, 0.95, 5, coeffs=sets[k])
+        torch.cuda.synchronize()
+        for a, b in zip(_bits(P) + _bits(M), _bits(P2) + _bits(M2)):
+            assert np.array_equal(a, b)
+        for i, c in enumerate(case):
+            rp, rb, _ = oracle.muon_matrix_step(c["params"].as_f64(), c["grad"].as_f64(),
+                                                c["momentum"].astype(np.float64), 0.02, 0.95, 5,
+                                                coeffs=sets[set_of[i]])
+            e = check_update(c["params"].as_f64(), from_device(P[i]), rp, dtype, tol, label=f"set {set_of[i]} #{i}")
+            assert e <= tol, (dtype, i, e)
+
+
+def test_eps_and_rms_target_options(nsa):
+    # A non-default epsilon large enough to change the normalisation (eps =
+    # 0.1 against ||u||_F of about 0.3 here) and a non-default RMS target.
+    for dtype, tol in (("f32", F32_TOL), ("bf16", BF16_TOL)):
+        case = workloads.random_case(31, [(192, 320), (320, 192), (100, 60)], dtype, params_init="zero")
+        p1, m1 = run_case(nsa, case, dtype, 0.02, 0.95, 5, eps=0.1, rms_target=0.35)
+        ref = oracle_case(case, 0.02, 0.95, 5, eps=0.1, rms_target=0.35)
+        assert_parity(case, dtype, p1, m1, ref, tol)
+        # the options matter: the default eps gives a different update
+        other = oracle_case(case, 0.02, 0.95, 5, rms_target=0.35)
+        assert rel_fro(ref[0][0], other[0][0]) > 10 * tol

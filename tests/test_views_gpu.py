@@ -14,7 +14,7 @@ import numpy as np
 import pytest
 
 import workloads
-from gpu_helpers import BF16_TOL, F32_TOL, MOM_TOL, check_update, from_device, oracle_case, rel_fro
+from gpu_helpers import BF16_TOL, F32_TOL, MOM_TOL, check_momentum, check_update, from_device, oracle_case
 
 pytestmark = pytest.mark.gpu
 
@@ -59,8 +59,8 @@ def test_ns_dtype_against_oracle(nsa, tensors, ns, tol):
     worst = 0.0
     for i, (c, (rp, rb, _)) in enumerate(zip(case, ref)):
         p0 = c["params"].as_f64()
-        e = check_update(p0, from_device(P[i]), rp, tensors, tol)
-        em = rel_fro(from_device(M[i]), rb.astype(np.float32))
+        e = check_update(p0, from_device(P[i]), rp, tensors, tol, label=f"{ns} NS #{i}")
+        em = check_momentum(from_device(M[i]), rb, label=f"#{i}")
         worst = max(worst, e)
         assert e <= tol, (i, SHAPES[i], e)
         assert em <= MOM_TOL, (i, SHAPES[i], em)
@@ -157,9 +157,9 @@ def test_views_against_oracle(nsa):
     import oracle
     for (p0, g0, m0), (a, _, c) in zip(before, vs):
         rp, rb, _ = oracle.muon_matrix_step(p0, g0, m0, 0.02, 0.95, 5)
-        e = check_update(p0, from_device(a), rp, "bf16", BF16_TOL)
+        e = check_update(p0, from_device(a), rp, "bf16", BF16_TOL, label="view")
         assert e <= BF16_TOL, (p0.shape, e)
-        assert rel_fro(from_device(c), rb.astype(np.float32)) <= MOM_TOL
+        assert check_momentum(from_device(c), rb, label="view") <= MOM_TOL
 
 
 def test_views_at_model_shapes(nsa):
@@ -200,6 +200,6 @@ def test_views_of_fp32_masters_with_bf16_ns(nsa):
     for (p0, g0, m0), (a, _, c), (ca, _, cc) in zip(before, vs, copies):
         assert torch.equal(a, ca) and torch.equal(c, cc)
         rp, rb, _ = oracle.muon_matrix_step(p0, g0, m0, 0.02, 0.95, 5)
-        e = check_update(p0, from_device(a), rp, "f32", BF16_TOL)
+        e = check_update(p0, from_device(a), rp, "f32", BF16_TOL, label="fp32 master view")
         assert e <= BF16_TOL, (p0.shape, e)
-        assert rel_fro(from_device(c), rb.astype(np.float32)) <= MOM_TOL
+        assert check_momentum(from_device(c), rb, label="view") <= MOM_TOL
