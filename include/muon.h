@@ -88,6 +88,8 @@ enum {
 #define MUON_MAX_NS_STEPS 64
 #define MUON_MAX_DIM (1 << 20)
 #define MUON_DEFAULT_BATCH_CAP ((size_t)1 << 29)
+/* Size of the static device workspace of muon_step_noalloc (per GPU). */
+#define MUON_STATIC_WORKSPACE_BYTES ((size_t)512 << 20)
 
 /* Forms of the NS polynomial step on the bf16 path (muon_options.poly_form).
  *   MUON_POLY_SQUARE (default): with c != 0 the polynomial completed to a
@@ -193,6 +195,21 @@ int muon_group_step(void* const* params, const void* const* grads, float* const*
  * matrices first). opts may be NULL. Matrices must not alias each other. */
 int muon_step(const muon_matrix* mats, int num, float lr, float beta, int ns_steps,
               muon_dtype dtype, const muon_options* opts, void* stream);
+
+/* muon_step for callers that cannot allocate device memory (code under HIP
+ * graph capture, tight serving loops, harnesses that forbid hipMalloc): the
+ * same step, arguments and results as muon_step (bitwise: batches never
+ * change a matrix's result), with the workspace in a static device array of
+ * MUON_STATIC_WORKSPACE_BYTES that the library holds on each GPU it runs on
+ * until the process ends, instead of a stream-ordered allocation. It calls
+ * no device allocation routine. Batches are sized to fit the array; a
+ * matrix whose workspace alone does not fit (e.g. 7168 x 18432 bf16) is
+ * rejected with MUON_ERR_INVALID_ARGUMENT naming it, before anything is
+ * launched. Every call on a GPU shares that GPU's array and leaves its
+ * contents behind: calls that overlap in time on one GPU (other streams,
+ * other threads) race on it and must be ordered by the caller. */
+int muon_step_noalloc(const muon_matrix* mats, int num, float lr, float beta, int ns_steps,
+                      muon_dtype dtype, const muon_options* opts, void* stream);
 
 /* One logical matrix of a physical parameter, as a zero-copy strided view
  * (section 6.6: the model adapter defines the matrices Muon sees inside a

@@ -28,7 +28,7 @@ from typing import Iterable, List, Optional, Sequence, Tuple
 
 import torch  # loaded first: libmuon then binds to torch's HIP runtime
 
-__all__ = ["MuonError", "matrix_layout", "muon_group_step", "muon_step", "muon_step_views", "muon_orthogonalize", "plan_query",
+__all__ = ["MuonError", "matrix_layout", "muon_group_step", "muon_step", "muon_step_noalloc", "muon_step_views", "muon_orthogonalize", "plan_query",
            "profile_enable", "profile_read", "version", "library_path", "load"]
 
 MUON_F32, MUON_BF16 = 0, 1
@@ -75,7 +75,8 @@ class ProfileEntry(ctypes.Structure):
 
 
 _LIB = None
-SYMBOLS = ("muon_default_options", "muon_group_step", "muon_step", "muon_step_views", "muon_orthogonalize",
+SYMBOLS = ("muon_default_options", "muon_group_step", "muon_step", "muon_step_noalloc", "muon_step_views",
+           "muon_orthogonalize",
            "muon_plan_query", "muon_status_string", "muon_last_error", "muon_version",
            "muon_profile_enable", "muon_profile_read")
 
@@ -101,6 +102,8 @@ def load() -> ctypes.CDLL:
     L.muon_group_step.restype = i
     L.muon_step.argtypes = [ctypes.POINTER(Matrix), i, f, f, i, i, ctypes.POINTER(Options), vp]
     L.muon_step.restype = i
+    L.muon_step_noalloc.argtypes = [ctypes.POINTER(Matrix), i, f, f, i, i, ctypes.POINTER(Options), vp]
+    L.muon_step_noalloc.restype = i
     L.muon_step_views.argtypes = [ctypes.POINTER(MatrixView), i, f, f, i, i, ctypes.POINTER(Options), vp]
     L.muon_step_views.restype = i
     L.muon_orthogonalize.argtypes = [ctypes.POINTER(vp), ctypes.POINTER(vp), i, i, i, i, i,
@@ -292,6 +295,19 @@ def muon_step(mats: Iterable[Tuple[torch.Tensor, torch.Tensor, torch.Tensor]], l
     poly_form: "square" (default) or "direct"; coeff_sets: a list of per-step
     coefficient tables with coeff_set_of: one set index per triple, which
     applies to every matrix the triple holds)."""
+    _step("muon_step", mats, lr, beta, ns_steps, stream, options)
+
+
+def muon_step_noalloc(mats: Iterable[Tuple[torch.Tensor, torch.Tensor, torch.Tensor]], lr: float,
+                      beta: float = 0.95, ns_steps: int = 5, stream=None, **options) -> None:
+    """C `muon_step_noalloc`: muon_step with the workspace in the library's
+    static device array (no device allocation; calls that overlap on one
+    GPU race on it). Arguments as muon_step."""
+    _step("muon_step_noalloc", mats, lr, beta, ns_steps, stream, options)
+
+
+def _step(entry: str, mats, lr: float, beta: float, ns_steps: int, stream, options: dict) -> None:
+    """muon_step / muon_step_noalloc: marshals the triples and calls `entry`."""
     rows = []
     dt = None
     per_entry = options.pop("coeff_set_of", None)
@@ -319,7 +335,7 @@ def muon_step(mats: Iterable[Tuple[torch.Tensor, torch.Tensor, torch.Tensor]], l
         return
     o, keep = _options(ns_steps=ns_steps, set_of_matrix=set_of, **options)
     arr = (Matrix * len(rows))(*rows)
-    _check(load().muon_step(arr, len(rows), lr, beta, ns_steps, dt, ctypes.byref(o), _stream(stream)))
+    _check(getattr(load(), entry)(arr, len(rows), lr, beta, ns_steps, dt, ctypes.byref(o), _stream(stream)))
     del keep
 
 

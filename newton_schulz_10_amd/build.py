@@ -21,7 +21,7 @@ INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libmuon.so")
 
-SOURCES = ["plan.cpp", "muon_api.cpp", "elementwise.hip", "gemm_bf16.hip", "gemm_f32.hip"]
+SOURCES = ["plan.cpp", "muon_api.cpp", "elementwise.hip", "gemm_bf16.hip", "gemm_f32.hip", "scratch.hip"]
 ARCH = os.environ.get("MUON_OFFLOAD_ARCH", "gfx950")
 
 

@@ -159,6 +159,10 @@ hipError_t launch_apply(const EwMats& mats, const ApplyArgs& a, int p_bf16, int 
 hipError_t launch_gemm_bf16(GemmRole role, const GemmArgs& g, hipStream_t s);
 hipError_t launch_gemm_f32(GemmRole role, const GemmArgs& g, hipStream_t s);
 
+// Device address and size of the calling thread's current device's static
+// workspace (scratch.hip), resolved on the first call per device.
+hipError_t static_workspace(void** ptr, size_t* bytes);
+
 // Algorithmic flops of one launch (nominal: a dense product counts
 // 2*M*N*K even where symmetry halves the executed work).
 double gemm_flops(GemmRole role, const GemmArgs& g);

@@ -166,8 +166,12 @@ int fit_units(const muon_options& o) {
   return n;
 }
 
+// The launch sequence of one call. With use_static, the workspace is the
+// current device's static array (muon_step_noalloc: batches sized to fit
+// it, nothing allocated or freed); otherwise one stream-ordered allocation
+// from the library's pool, freed stream-ordered at the end.
 int run(const std::vector<MatRef>& mats, float lr, float beta, int ns_steps, muon_dtype dtype,
-        const muon_options& o, bool orthogonalize_only, hipStream_t stream) {
+        const muon_options& o, bool orthogonalize_only, hipStream_t stream, bool use_static = false) {
   if (mats.empty()) return MUON_OK;
   PhaseRange call_range(std::string(orthogonalize_only ? "muon_orthogonalize" : "muon_step") + " (" +
                    std::to_string(mats.size()) + " matrices)");
@@ -180,25 +184,32 @@ int run(const std::vector<MatRef>& mats, float lr, float beta, int ns_steps, muo
   Plan plan;
   std::string err;
   const int* set_of = o.num_coeff_sets > 0 ? o.coeff_set_of : nullptr;
-  int rc = build_plan(rows.data(), cols.data(), num, ns, o.batch_cap_elems, fit_units(o), plan, err, set_of,
-                      o.num_coeff_sets);
-  if (rc) return fail(rc, err);
-
-  if (const char* f = std::getenv("MUON_TEST_FAIL_ALLOC"))
-    if (f[0] == '1') return fail(MUON_ERR_OUT_OF_MEMORY, "workspace allocation failed (MUON_TEST_FAIL_ALLOC=1)");
-
-  int dev = 0;
-  hipError_t e = hipGetDevice(&dev);
-  if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
-  hipMemPool_t pool;
-  e = get_pool(dev, &pool);
-  if (e != hipSuccess) return hip_fail(e, "hipMemPoolCreate");
+  hipError_t e = hipSuccess;
   void* ws = nullptr;
-  e = hipMallocFromPoolAsync(&ws, plan.workspace_bytes, pool, stream);
-  if (e != hipSuccess) {
-    (void)hipGetLastError();
-    return fail(MUON_ERR_OUT_OF_MEMORY, std::string("workspace allocation of ") +
-                std::to_string(plan.workspace_bytes) + " bytes failed: " + hipGetErrorString(e));
+  size_t static_bytes = 0;
+  if (use_static) {
+    e = static_workspace(&ws, &static_bytes);
+    if (e != hipSuccess) return hip_fail(e, "static workspace (hipGetSymbolAddress)");
+  }
+  int rc = build_plan(rows.data(), cols.data(), num, ns, o.batch_cap_elems, use_static ? 0 : fit_units(o), plan,
+                      err, set_of, o.num_coeff_sets, static_bytes);
+  if (rc) return fail(rc, use_static ? err + " (the static workspace of muon_step_noalloc)" : err);
+
+  if (!use_static) {
+    if (const char* f = std::getenv("MUON_TEST_FAIL_ALLOC"))
+      if (f[0] == '1') return fail(MUON_ERR_OUT_OF_MEMORY, "workspace allocation failed (MUON_TEST_FAIL_ALLOC=1)");
+    int dev = 0;
+    e = hipGetDevice(&dev);
+    if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+    hipMemPool_t pool;
+    e = get_pool(dev, &pool);
+    if (e != hipSuccess) return hip_fail(e, "hipMemPoolCreate");
+    e = hipMallocFromPoolAsync(&ws, plan.workspace_bytes, pool, stream);
+    if (e != hipSuccess) {
+      (void)hipGetLastError();
+      return fail(MUON_ERR_OUT_OF_MEMORY, std::string("workspace allocation of ") +
+                  std::to_string(plan.workspace_bytes) + " bytes failed: " + hipGetErrorString(e));
+    }
   }
 
   const bool bf16 = ns == MUON_BF16;           // NS kernels: bf16 MFMA, else fp32
@@ -367,8 +378,10 @@ int run(const std::vector<MatRef>& mats, float lr, float beta, int ns_steps, muo
     if (status) break;
   }
 
-  hipError_t ef = hipFreeAsync(ws, stream);
-  if (status == MUON_OK && ef != hipSuccess) status = hip_fail(ef, "hipFreeAsync");
+  if (!use_static) {
+    hipError_t ef = hipFreeAsync(ws, stream);
+    if (status == MUON_OK && ef != hipSuccess) status = hip_fail(ef, "hipFreeAsync");
+  }
   return status;
 }
 
@@ -452,6 +465,28 @@ int muon_step(const muon_matrix* mats, int num, float lr, float beta, int ns_ste
     rc = validate_mats(v, dtype, false);
     if (rc) return rc;
     return run(v, lr, beta, ns_steps, dtype, o, false, static_cast<hipStream_t>(stream));
+  } catch (const std::exception& ex) {
+    return fail(MUON_ERR_HIP, std::string("internal error: ") + ex.what());
+  } catch (...) {
+    return fail(MUON_ERR_HIP, "internal error");
+  }
+}
+
+int muon_step_noalloc(const muon_matrix* mats, int num, float lr, float beta, int ns_steps, muon_dtype dtype,
+                      const muon_options* opts, void* stream) {
+  try {
+    g_err.clear();
+    if (num < 0) return fail(MUON_ERR_INVALID_ARGUMENT, "num < 0");
+    if (num > 0 && !mats) return fail(MUON_ERR_INVALID_ARGUMENT, "mats is NULL");
+    muon_options o;
+    int rc = validate_common(lr, beta, ns_steps, dtype, opts, o);
+    if (rc) return rc;
+    std::vector<MatRef> v(num);
+    for (int i = 0; i < num; ++i)
+      v[i] = MatRef{mats[i].param, mats[i].grad, mats[i].momentum, mats[i].rows, mats[i].cols, mats[i].cols};
+    rc = validate_mats(v, dtype, false);
+    if (rc) return rc;
+    return run(v, lr, beta, ns_steps, dtype, o, false, static_cast<hipStream_t>(stream), true);
   } catch (const std::exception& ex) {
     return fail(MUON_ERR_HIP, std::string("internal error: ") + ex.what());
   } catch (...) {
