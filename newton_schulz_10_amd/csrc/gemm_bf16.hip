@@ -324,13 +324,10 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& g, int mat, int I, int
     for (int f = 0; f < 8; ++f) read_one(kt, ks, f, rf, cf);
   };
 
+  // Accumulators: the first K-step's MFMAs take a zero C operand (an
+  // inline constant), so they need no initialisation.
   f32x16 acc[4][4];  // [column block][row block]
-#pragma unroll
-  for (int a = 0; a < 4; ++a)
-#pragma unroll
-    for (int b = 0; b < 4; ++b)
-#pragma unroll
-      for (int v = 0; v < 16; ++v) acc[a][b][v] = 0.0f;
+  const f32x16 zero16 = {};
 
   // Vector-memory issue order (the queue completes in order). Slab j's
   // compute issues fill(j+3) in two halves around its barrier:
@@ -351,12 +348,13 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& g, int mat, int I, int
   // step's NLh fill loads spread over MFMAs 8..15, so no MFMA carries more
   // than one of them. Issued in bursts, reads and loads queue up in front
   // of the next MFMA and stall the wave's (in-order) issue.
-  auto mfma_step = [&](int cur, auto hook) {
+  auto mfma_step = [&](int cur, auto hook, auto first) {
 #pragma unroll
     for (int a = 0; a < 4; ++a) {
 #pragma unroll
       for (int b = 0; b < 4; ++b) {
-        acc[a][b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(cf[cur][a], rf[cur][b], acc[a][b], 0, 0, 0);
+        acc[a][b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(cf[cur][a], rf[cur][b],
+                                                            decltype(first)::value ? zero16 : acc[a][b], 0, 0, 0);
         __builtin_amdgcn_sched_barrier(0);
         hook(4 * a + b);
         __builtin_amdgcn_sched_barrier(0);
@@ -381,13 +379,14 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& g, int mat, int I, int
   //   3: the last slab, no barrier.
   // Every read of a stage is issued and completed (lgkmcnt(0)) before the
   // barrier after which that stage is filled again.
-  auto slab = [&](int kt, auto mode) {
+  auto slab = [&](int kt, auto mode, auto first) {
     constexpr int M = decltype(mode)::value;
+    using F0 = std::false_type;
     if constexpr (M < 3) {
       mfma_step(0, [&](int i) {
         if (i < 8) read_one(kt, 1, i, rf[1], cf[1]);
         if constexpr (M == 0) fill_slot(kt + 3, 0, i);
-      });
+      }, first);
       // This wave's fill of slab kt+1 and its LDS reads have completed;
       // after the barrier, every wave's have, and stage (kt+3) % 4's last
       // readers (slab kt-1) are long done.
@@ -396,20 +395,22 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& g, int mat, int I, int
       mfma_step(1, [&](int i) {
         if (i < 8) read_one(kt + 1, 0, i, rf[0], cf[0]);
         if constexpr (M == 0) fill_slot(kt + 3, 1, i);
-      });
+      }, F0{});
     } else {
       mfma_step(0, [&](int i) {
         if (i < 8) read_one(kt, 1, i, rf[1], cf[1]);
-      });
-      mfma_step(1, [](int) {});
+      }, F0{});
+      mfma_step(1, [](int) {}, F0{});
     }
   };
-  // K >= 128 (m_pad is a positive multiple of 128), so nk >= 4.
-  for (int kt = 0; kt < last - 2; ++kt) slab(kt, std::integral_constant<int, 0>{});
-  slab(last - 2, std::integral_constant<int, 1>{});
-  slab(last - 1, std::integral_constant<int, 2>{});
+  // K >= 128 (m_pad is a positive multiple of 128), so nk >= 4 and slab 0
+  // is a steady one (0 < last - 2).
+  slab(0, std::integral_constant<int, 0>{}, std::true_type{});
+  for (int kt = 1; kt < last - 2; ++kt) slab(kt, std::integral_constant<int, 0>{}, std::false_type{});
+  slab(last - 2, std::integral_constant<int, 1>{}, std::false_type{});
+  slab(last - 1, std::integral_constant<int, 2>{}, std::false_type{});
   const int claim = claim_issue(cl, tid);
-  slab(last, std::integral_constant<int, 3>{});
+  slab(last, std::integral_constant<int, 3>{}, std::false_type{});
 
   // ---- epilogue ----------------------------------------------------------
   {
@@ -799,21 +800,17 @@ __device__ __forceinline__ void gemm_diag_tile(const GemmArgs& g, int mat, int I
       const bf16x8 v = *reinterpret_cast<const bf16x8*>(S + r * BK + ((ch ^ kswz(r)) * 8));
       if (is_c) cf[idx] = v; else rf[idx] = v;
     };
-    f32x16 acc[4][4];
-#pragma unroll
-    for (int a = 0; a < 4; ++a)
-#pragma unroll
-      for (int b = 0; b < 4; ++b)
-#pragma unroll
-        for (int v = 0; v < 16; ++v) acc[a][b][v] = 0.0f;
+    f32x16 acc[4][4];   // the first K-step takes a zero C operand
+    const f32x16 zero16 = {};
     bf16x8 rf[2][4], cf[2][4];
 #pragma unroll
     for (int f = 0; f < NR; ++f) read_one(0, 0, f, rf[0], cf[0]);
-    auto mstep = [&](int cur, auto hook) {
+    auto mstep = [&](int cur, auto hook, auto first) {
 #pragma unroll
       for (int i = 0; i < NM; ++i) {
         const int a = diag_a(KIND, i), b = diag_b(KIND, i);
-        acc[a][b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(cf[cur][a], rf[cur][b], acc[a][b], 0, 0, 0);
+        acc[a][b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(cf[cur][a], rf[cur][b],
+                                                            decltype(first)::value ? zero16 : acc[a][b], 0, 0, 0);
         __builtin_amdgcn_sched_barrier(0);
         hook(i);
         __builtin_amdgcn_sched_barrier(0);
@@ -826,31 +823,33 @@ __device__ __forceinline__ void gemm_diag_tile(const GemmArgs& g, int mat, int I
     };
     // Modes as in gemm_tile: 0 fills slab kt+3, 1 and 2 (kt = last-2,
     // last-1) fill nothing and wait for fewer loads, 3 is the last slab.
-    auto slab = [&](int kt, auto mode) {
+    auto slab = [&](int kt, auto mode, auto first) {
       constexpr int M = decltype(mode)::value;
+      using F0 = std::false_type;
       if constexpr (M < 3) {
         mstep(0, [&](int i) {
           if (i < NR) read_one(kt, 1, i, rf[1], cf[1]);
           if constexpr (M == 0) fill_slot(kt + 3, 0, i);
-        });
+        }, first);
         __builtin_amdgcn_s_waitcnt(vmcnt_lgkm0(M == 0 ? NL + NLh : (M == 1 ? NL : 0)));
         lds_barrier();
         mstep(1, [&](int i) {
           if (i < NR) read_one(kt + 1, 0, i, rf[0], cf[0]);
           if constexpr (M == 0) fill_slot(kt + 3, 1, i);
-        });
+        }, F0{});
       } else {
         mstep(0, [&](int i) {
           if (i < NR) read_one(kt, 1, i, rf[1], cf[1]);
-        });
-        mstep(1, [](int) {});
+        }, F0{});
+        mstep(1, [](int) {}, F0{});
       }
     };
-    for (int kt = 0; kt < last - 2; ++kt) slab(kt, std::integral_constant<int, 0>{});
-    slab(last - 2, std::integral_constant<int, 1>{});
-    slab(last - 1, std::integral_constant<int, 2>{});
+    slab(0, std::integral_constant<int, 0>{}, std::true_type{});
+    for (int kt = 1; kt < last - 2; ++kt) slab(kt, std::integral_constant<int, 0>{}, std::false_type{});
+    slab(last - 2, std::integral_constant<int, 1>{}, std::false_type{});
+    slab(last - 1, std::integral_constant<int, 2>{}, std::false_type{});
     claim = claim_issue(cl, tid);
-    slab(last, std::integral_constant<int, 3>{});
+    slab(last, std::integral_constant<int, 3>{}, std::false_type{});
 
     __builtin_amdgcn_s_waitcnt(0x0070);  // vmcnt(0) lgkmcnt(0): stages no longer read
     lds_barrier();
