@@ -70,6 +70,9 @@ def parse():
     ap.add_argument("--mfma", metavar="MFMA_DIR",
                     help="with --summarize: a --pmc MfmaFlopsBF16 MfmaUtil run, for executed MFMA flops "
                          "and MFMA busy time per kernel")
+    ap.add_argument("--clock", metavar="CLOCK_DIR",
+                    help="with --summarize: a --pmc GRBM_GUI_ACTIVE --kernel-trace run, for each kernel's "
+                         "effective shader clock (GPU-busy cycles over the dispatch's duration)")
     return ap.parse_args()
 
 
@@ -146,13 +149,21 @@ class ClockSampler:
             self.error = f"{type(e).__name__}: {e}"
 
     def _read(self):
+        """(GFX clock MHz, socket power W) from the GPU metrics table: the
+        mean of the per-XCD current gfx clocks (else the averaged gfx clock),
+        and the current socket power (else the averaged one)."""
         smi = self._smi
-        clk = smi.amdsmi_get_clock_info(self._h, smi.AmdSmiClkType.GFX)["clk"]
-        pw = smi.amdsmi_get_power_info(self._h)
-        w = pw.get("current_socket_power", "N/A")
-        if not isinstance(w, (int, float)):
-            w = pw.get("average_socket_power", None)
-        return float(clk), (float(w) if isinstance(w, (int, float)) else None)
+        m = smi.amdsmi_get_gpu_metrics_info(self._h)
+
+        def num(v):
+            return float(v) if isinstance(v, (int, float)) and 0 < v < 65535 else None
+
+        clks = [num(v) for v in (m.get("current_gfxclks") or []) if num(v)]
+        clk = sum(clks) / len(clks) if clks else num(m.get("average_gfxclk_frequency"))
+        w = num(m.get("current_socket_power")) or num(m.get("average_socket_power"))
+        if clk is None:
+            raise RuntimeError("no gfx clock in the GPU metrics table")
+        return clk, w
 
     def start(self):
         import threading
@@ -183,7 +194,9 @@ class ClockSampler:
         clk = [c for c, _ in self.samples]
         pw = [p for _, p in self.samples if p is not None]
         out = {"sclk_mhz_mean": sum(clk) / len(clk), "sclk_mhz_min": min(clk), "sclk_mhz_max": max(clk),
-               "samples": len(clk), "source": "amdsmi GFX clock, sampled every 10 ms during the timed steps"}
+               "samples": len(clk),
+               "source": "amdsmi GPU metrics (mean of the per-XCD current gfx clocks), sampled every 10 ms "
+                         "during the timed steps; the kernels' own mean clock is in roofline.clock_mhz_profiled"}
         if pw:
             out["socket_power_w_mean"] = sum(pw) / len(pw)
         return out
@@ -229,8 +242,38 @@ def _counter_per_kind(rows, counter):
     return {k: sum(v) / len(v) for k, v in kinds.items()}, copy
 
 
-def summarize(trace_dir, fetch_dir, write_dir, workload, mfma_dir=None):
+def _clock_per_kind(d):
+    """Effective shader clock (MHz) per kernel kind: GRBM_GUI_ACTIVE (GPU-busy
+    cycles, summed by the tool over the XCDs) / XCD count / dispatch time."""
+    rows = _read_csvs(d, "counter_collection.csv")
+    trace = {r["Dispatch_Id"]: int(r["End_Timestamp"]) - int(r["Start_Timestamp"])
+             for r in _read_csvs(d, "kernel_trace.csv")}
+    xcc = 1
+    for r in _read_csvs(d, "agent_info.csv"):
+        if r.get("Name", "").startswith("gfx") and int(r.get("Num_Xcc") or 0) > 0:
+            xcc = int(r["Num_Xcc"])
+    cyc, ns = {}, {}
+    for r in rows:
+        if r["Counter_Name"] != "GRBM_GUI_ACTIVE" or r["Dispatch_Id"] not in trace:
+            continue
+        k = kernel_kind(r["Kernel_Name"])
+        if not k:
+            continue
+        cyc[k] = cyc.get(k, 0.0) + float(r["Counter_Value"]) / xcc
+        ns[k] = ns.get(k, 0.0) + trace[r["Dispatch_Id"]]
+    # Dispatches shorter than about 20 us are dominated by the counter's
+    # start/stop granularity: no clock for those kinds.
+    n = {}
+    for r in rows:
+        if r["Counter_Name"] == "GRBM_GUI_ACTIVE" and r["Dispatch_Id"] in trace and kernel_kind(r["Kernel_Name"]):
+            k = kernel_kind(r["Kernel_Name"])
+            n[k] = n.get(k, 0) + 1
+    return {k: cyc[k] / ns[k] * 1e3 for k in cyc if ns.get(k) and ns[k] / n[k] >= 20e3}
+
+
+def summarize(trace_dir, fetch_dir, write_dir, workload, mfma_dir=None, clock_dir=None):
     stats = _read_csvs(trace_dir, "kernel_stats.csv")
+    clock = _clock_per_kind(clock_dir) if clock_dir else {}
     mflops, mutil = {}, {}
     if mfma_dir:
         rows = _read_csvs(mfma_dir, "counter_collection.csv")
@@ -257,6 +300,8 @@ def summarize(trace_dir, fetch_dir, write_dir, workload, mfma_dir=None):
         if mfma_dir:
             e["mfma_bf16_flops_per_launch"] = mflops.get(k)
             e["mfma_busy_pct"] = mutil.get(k)
+        if clock_dir:
+            e["clock_mhz"] = clock.get(k)
     dom = max(kinds, key=lambda k: kinds[k]["total_ns"])
     data = {"workload": workload, "source_sha256": source_hash(),
             "calibration": {"copy_bytes": COPY_CALIB_BYTES, "fetch_kib_read": fcopy, "write_kib_read": wcopy,
@@ -273,24 +318,35 @@ def summarize(trace_dir, fetch_dir, write_dir, workload, mfma_dir=None):
         for c, d in (("FETCH_SIZE", "<FETCH_DIR>"), ("WRITE_SIZE", "<WRITE_DIR>")):
             f.write(f"rocprofv3 --pmc {c} --output-format csv -d {d} -o pmc -- "
                     f"python3 $REPO/bench.py --workload {workload} --steps 1 --warmup 0 --cpu-seconds 0 --copy-calib\n")
+        extra = ""
         if mfma_dir:
             f.write(f"rocprofv3 --pmc MfmaFlopsBF16 MfmaUtil --output-format csv -d <MFMA_DIR> -o pmc -- "
                     f"python3 $REPO/bench.py --workload {workload} --steps 1 --warmup 0 --cpu-seconds 0\n")
-            f.write(f"python3 $REPO/bench.py --summarize <TRACE_DIR> <FETCH_DIR> <WRITE_DIR> --mfma <MFMA_DIR> "
-                    f"--workload {workload}\n```\n\n")
-        else:
-            f.write(f"python3 $REPO/bench.py --summarize <TRACE_DIR> <FETCH_DIR> <WRITE_DIR> --workload {workload}\n```\n\n")
+            extra += " --mfma <MFMA_DIR>"
+        if clock_dir:
+            f.write(f"rocprofv3 --pmc GRBM_GUI_ACTIVE --kernel-trace --output-format csv -d <CLOCK_DIR> -o pmc -- "
+                    f"python3 $REPO/bench.py --workload {workload} --steps 1 --warmup 1 --cpu-seconds 0\n")
+            extra += " --clock <CLOCK_DIR>"
+        f.write(f"python3 $REPO/bench.py --summarize <TRACE_DIR> <FETCH_DIR> <WRITE_DIR>{extra} "
+                f"--workload {workload}\n```\n\n")
         f.write(f"Counter scale: a {COPY_CALIB_BYTES >> 20} MiB device copy reads FETCH_SIZE {fcopy:.0f} KiB "
                 f"(x{f_scale:.3f}) and WRITE_SIZE {wcopy:.0f} KiB (x{w_scale:.3f}).\n\n")
         if mfma_dir:
             f.write("MFMA columns: executed bf16 MFMA flops per launch (MfmaFlopsBF16, the MFMA op counter x 512), "
                     "the same over the launch's average duration, and MFMA busy time over GPU-active time "
                     "summed over all SIMDs (MfmaUtil).\n\n")
+        if clock_dir:
+            f.write("Clock column: GPU-busy cycles (GRBM_GUI_ACTIVE, summed over the XCDs by the tool, divided by "
+                    "their number) over each dispatch's duration, i.e. the mean shader clock while the kernel "
+                    "ran.\n\n")
         head = "| kernel | launches | avg ms | HBM read GB/launch | HBM write GB/launch |"
         rule = "|---|---|---|---|---|"
         if mfma_dir:
             head += " executed MFMA TFLOP/launch | executed TFLOP/s | MFMA busy % |"
             rule += "---|---|---|"
+        if clock_dir:
+            head += " clock MHz |"
+            rule += "---|"
         f.write(head + "\n" + rule + "\n")
         for k, e in sorted(kinds.items(), key=lambda kv: -kv[1]["total_ns"]):
             rd = e["hbm_read_bytes_per_launch"]
@@ -303,6 +359,9 @@ def summarize(trace_dir, fetch_dir, write_dir, workload, mfma_dir=None):
                 line += (f" {'-' if not fl else f'{fl / 1e12:.4f}'} |"
                          f" {'-' if rate is None else f'{rate:.1f}'} |"
                          f" {'-' if ut is None else f'{ut:.1f}'} |")
+            if clock_dir:
+                ck = e.get("clock_mhz")
+                line += f" {'-' if ck is None else f'{ck:.0f}'} |"
             f.write(line + "\n")
         f.write("\nMachine-readable copy (bench.py reads it while `source_sha256` matches the sources):\n\n")
         f.write("```json\n" + json.dumps(data, indent=1) + "\n```\n")
@@ -438,7 +497,7 @@ def cpu_baseline(w, budget_s):
 def main():
     args = parse()
     if args.summarize:
-        summarize(*args.summarize, args.workload, args.mfma)
+        summarize(*args.summarize, args.workload, args.mfma, args.clock)
         return
     if args.gpus != 1:
         print(f"bench.py measures one GPU: --gpus {args.gpus} is not supported (the library runs on "
@@ -512,6 +571,11 @@ def main():
             # MFMA flops per launch and MFMA busy time (rocprofv3).
             roof["executed_mfma_tflop_per_launch"] = summ["mfma_bf16_flops_per_launch"] / 1e12
             roof["mfma_busy_pct"] = summ.get("mfma_busy_pct")
+        if summ and summ.get("clock_mhz"):
+            # The kernel's mean shader clock in the committed counter run, and
+            # the bf16 peak at that clock (the spec peak assumes 2.4 GHz).
+            roof["clock_mhz_profiled"] = summ["clock_mhz"]
+            roof["frac_of_peak_at_clock"] = achieved / (peak * summ["clock_mhz"] / 2400.0)
     else:
         achieved = dv["bytes"] / (dv["total_ms"] * 1e-3) / 1e9
         roof = {"bound": "hbm", "achieved": achieved, "peak": PEAK_HBM_GBS, "unit": "GB/s",

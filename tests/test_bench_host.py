@@ -83,3 +83,40 @@ def test_summary_needs_the_calibration_copy(tmp_path, monkeypatch):
     _counters(wr, "WRITE_SIZE", [(UPD, 1.0)])
     with pytest.raises(SystemExit):
         bench.summarize(tr, fe, wr, "w_test")
+
+
+def test_summary_clock_column(tmp_path, monkeypatch):
+    # GRBM_GUI_ACTIVE comes summed over the XCDs: 8 XCDs x 1.8e6 busy cycles
+    # in a 1 ms dispatch is a 1800 MHz clock; dispatches under 20 us get none.
+    monkeypatch.setattr(bench, "PROFILES", str(tmp_path / "profiles"))
+    tr, fe, wr, ck = (str(tmp_path / d) for d in ("trace", "fetch", "write", "clock"))
+    _write(os.path.join(tr, "trace_kernel_stats.csv"),
+           [{"Name": UPD, "Calls": 2, "TotalDurationNs": 2e6},
+            {"Name": "muon::finalize_kernel(muon::FinalizeArgs)", "Calls": 1, "TotalDurationNs": 4e3}],
+           ["Name", "Calls", "TotalDurationNs"])
+    _counters(fe, "FETCH_SIZE", [(UPD, 1.0), (COPY, 524288.0)])
+    _counters(wr, "WRITE_SIZE", [(UPD, 1.0), (COPY, 1048576.0)])
+    fin = "muon::finalize_kernel(muon::FinalizeArgs)"
+    _counters(ck, "GRBM_GUI_ACTIVE", [(UPD, 8 * 1.8e6), (UPD, 8 * 1.6e6), (fin, 8 * 50e3)])
+    _write(os.path.join(ck, "pmc_kernel_trace.csv"),
+           [{"Dispatch_Id": 0, "Start_Timestamp": 0, "End_Timestamp": 1000000},
+            {"Dispatch_Id": 1, "Start_Timestamp": 0, "End_Timestamp": 1000000},
+            {"Dispatch_Id": 2, "Start_Timestamp": 0, "End_Timestamp": 4000}],
+           ["Dispatch_Id", "Start_Timestamp", "End_Timestamp"])
+    _write(os.path.join(ck, "pmc_agent_info.csv"), [{"Name": "gfx950", "Num_Xcc": 8}], ["Name", "Num_Xcc"])
+    bench.summarize(tr, fe, wr, "w_clk", None, ck)
+    e = bench.load_summary("w_clk", "ns_update")
+    assert e["clock_mhz"] == pytest.approx(1700.0)
+    assert bench.load_summary("w_clk", "norm_finalize")["clock_mhz"] is None
+    assert "| clock MHz |" in (tmp_path / "profiles" / "ns_update_w_clk.md").read_text()
+
+
+def test_executed_mfma_flops_model():
+    # 1408 x 2048: 5 full tile rows + a half row; Gram over the lower
+    # triangle with 36/64 diagonal tiles, Update over every tile.
+    e = bench.executed_mfma_flops(1408, 2048, 1, "square")
+    full, wide = 2 * 256 * 256, 2 * 128 * 512
+    assert e["ns_update"] == (5 * 8 * full + 4 * wide) * 1408
+    assert e["ns_gram"] == pytest.approx((10 * full + 5 * 36 / 64 * full + 3 * wide) * 2048)
+    assert bench.executed_mfma_flops(2048, 1408, 1) == e
+    assert bench.executed_mfma_flops(1408, 2048, 1, "direct")["ns_poly"] == (15 * full + 3 * wide) * 1408
