@@ -61,7 +61,7 @@ def parse():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="moe_bank_2048x1408")
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="oracle sample budget (0 = skip)")
-    ap.add_argument("--poly-form", default="square", choices=["square", "direct"],
+    ap.add_argument("--poly-form", default="square", choices=["square", "direct", "folded"],
                     help="bf16 form of the NS polynomial step (muon_options.poly_form)")
     ap.add_argument("--copy-calib", action="store_true",
                     help="also run one plain 1 GiB device copy (for HBM counter scaling)")
@@ -114,7 +114,7 @@ def executed_mfma_flops(rows: int, cols: int, ns_steps: int, poly_form: str = "s
         return (F * (F - 1) // 2 * full_tile + F * diag_frac * full_tile + wide_sym * wide_tile) * K
 
     gram = sym(np_, 36 / 64)
-    poly = sym(mp, 36 / 64 if poly_form == "square" else 1.0)
+    poly = sym(mp, 36 / 64 if poly_form == "square" else 1.0)   # an epilogue operand takes the full tile
     upd = (F * tu * full_tile + wide_upd * wide_tile) * mp
     return {"ns_gram": ns_steps * gram, "ns_poly": ns_steps * poly, "ns_update": ns_steps * upd}
 

@@ -104,8 +104,12 @@ enum {
  *     + c A A (b A added in fp32 from the A tile in the epilogue), X' = a X +
  *     B X (a X added in fp32 from the X tile in the epilogue); A, B and X'
  *     are each rounded once. About 7% slower on 1408 x 2048 matrices.
+ *   MUON_POLY_FOLDED: A = X X^T exact (no shift), B' = a I + b A + c A A
+ *     formed in fp32 from the A tile in Poly's epilogue and rounded once,
+ *     X' = B' X with no operand tile: the a X term rides in B' as in the
+ *     square form, but A's diagonal keeps its bits.
  * The float32 path always computes the direct form. */
-enum { MUON_POLY_DIRECT = 0, MUON_POLY_SQUARE = 1 };
+enum { MUON_POLY_DIRECT = 0, MUON_POLY_SQUARE = 1, MUON_POLY_FOLDED = 2 };
 
 /* Options. Section 6.2 of the paper makes the momentum rule, the NS step
  * count, coefficients and epsilon, and the update scale configurable
@@ -153,7 +157,8 @@ typedef struct muon_options {
                              FP32 optimizer state); the update is applied to
                              the fp32 params. MUON_F32 with dtype MUON_BF16:
                              bf16 tensors iterated in fp32.                   */
-  int poly_form;          /* MUON_POLY_SQUARE (default) or MUON_POLY_DIRECT     */
+  int poly_form;          /* MUON_POLY_SQUARE (default), MUON_POLY_DIRECT or
+                             MUON_POLY_FOLDED                                  */
   /* Per-parameter coefficient sets (section 6.2: per-parameter coefficient
    * sets reuse the same buffers). num_coeff_sets = 0 (default): `coeffs`
    * applies to every matrix. K > 0: coeffs must be NULL; coeff_sets is a

@@ -192,7 +192,7 @@ def _matrices(t: torch.Tensor, what: str, dtype: Optional[torch.dtype] = None) -
 _NS_DTYPES = {None: -1, torch.float32: MUON_F32, torch.bfloat16: MUON_BF16}
 
 
-_POLY_FORMS = {"direct": 0, "square": 1}
+_POLY_FORMS = {"direct": 0, "square": 1, "folded": 2}
 
 
 def _options(nesterov=True, momentum_form="ema", weight_decay=0.0, scale_rule="rms", rms_target=0.2,
@@ -292,7 +292,7 @@ def muon_step(mats: Iterable[Tuple[torch.Tensor, torch.Tensor, torch.Tensor]], l
     weight_decay, scale_rule, rms_target, eps, coeffs, batch_cap_elems,
     compute_units, ns_dtype: None for the tensors' dtype, or
     torch.bfloat16 to iterate float32 master tensors on bf16 MFMA;
-    poly_form: "square" (default) or "direct"; coeff_sets: a list of per-step
+    poly_form: "square" (default), "direct" or "folded"; coeff_sets: a list of per-step
     coefficient tables with coeff_set_of: one set index per triple, which
     applies to every matrix the triple holds)."""
     _step("muon_step", mats, lr, beta, ns_steps, stream, options)

@@ -309,12 +309,15 @@ int run(const std::vector<MatRef>& mats, float lr, float beta, int ns_steps, muo
       // Update B' X, with no operand tile; with c = 0 Poly forms a I + b A
       // + c A A with the A tile. The step's arithmetic is in double,
       // rounded once to float.
+      // MUON_POLY_FOLDED (and the square form with c = 0): Gram writes A,
+      // Poly a I + b A + c A A from the A tile, Update B' X.
       const bool square = bf16 && o.poly_form == MUON_POLY_SQUARE;
+      const bool folded = bf16 && (o.poly_form == MUON_POLY_FOLDED || (square && g.cc == 0.0f));
       const bool shifted = square && g.cc != 0.0f;
       const double beta_sq = shifted ? (double)g.cb / (2.0 * (double)g.cc) : 0.0;
       const float gram_diag = (float)beta_sq;
       const float poly_diag = shifted ? (float)((double)g.ca - (double)g.cb * (double)g.cb / (4.0 * (double)g.cc))
-                                      : (square ? g.ca : 0.0f);
+                                      : (folded ? g.ca : 0.0f);
       const GemmRole roles[3] = {kGram, kPoly, kUpdate};
       const char* names[3] = {"ns_gram", "ns_poly", "ns_update"};
       for (int r = 0; r < 3; ++r) {
@@ -331,7 +334,7 @@ int run(const std::vector<MatRef>& mats, float lr, float beta, int ns_steps, muo
         // zeroed by the compact kernel.
         g.sched = (skip_zero && r == 0) ? sched : nullptr;
         g.poly_operand = shifted ? 0 : 1;
-        g.update_operand = (bf16 && !square) ? 1 : 0;
+        g.update_operand = (bf16 && !square && !folded) ? 1 : 0;
         const bool apply_here = fused_apply && r == 2 && k + 1 == ns_steps;
         g.ptab = apply_here ? ptab : nullptr;
         g.alpha = apply_alpha;

@@ -205,8 +205,9 @@ int check_options(const muon_options& o, int ns_steps, std::string& err) {
         return MUON_ERR_INVALID_ARGUMENT;
       }
   }
-  if (o.poly_form != MUON_POLY_DIRECT && o.poly_form != MUON_POLY_SQUARE) {
-    err = "options.poly_form must be MUON_POLY_DIRECT or MUON_POLY_SQUARE"; return MUON_ERR_INVALID_ARGUMENT;
+  if (o.poly_form != MUON_POLY_DIRECT && o.poly_form != MUON_POLY_SQUARE && o.poly_form != MUON_POLY_FOLDED) {
+    err = "options.poly_form must be MUON_POLY_DIRECT, MUON_POLY_SQUARE or MUON_POLY_FOLDED";
+    return MUON_ERR_INVALID_ARGUMENT;
   }
   if (o.num_coeff_sets < 0) { err = "options.num_coeff_sets must be >= 0"; return MUON_ERR_INVALID_ARGUMENT; }
   if (o.num_coeff_sets > 0) {

@@ -138,7 +138,9 @@ int main() {
     muon_options o;
     default_options(o);
     CHECK(o.poly_form == MUON_POLY_SQUARE && o.num_coeff_sets == 0);
-    o.poly_form = 2;
+    o.poly_form = MUON_POLY_FOLDED;
+    CHECK(check_options(o, 5, err) == MUON_OK);
+    o.poly_form = 3;
     CHECK(check_options(o, 5, err) == MUON_ERR_INVALID_ARGUMENT);
     default_options(o);
     o.num_coeff_sets = 1;

@@ -172,12 +172,18 @@ def oracle_case(case: List[dict], lr: float, beta: float, ns_steps: int, **opts)
     return out
 
 
+FORM_NAMES = ("square", "direct", "folded")
+
+
 def summary_lines(records: Sequence[dict]) -> List[str]:
-    """One line per test: comparisons, worst err / raw / tile (update and
+    """One line per test (per test and polynomial form, where a comparison's
+    label names the form): comparisons, worst err / raw / tile (update and
     output comparisons) and the worst momentum error."""
     by_test = {}
     for r in records:
-        by_test.setdefault(r["test"], []).append(r)
+        form = r["label"].split(" ", 1)[0] if r["label"] else ""
+        key = f"{r['test']} [{form}]" if form in FORM_NAMES and r["kind"] != "momentum" else r["test"]
+        by_test.setdefault(key, []).append(r)
     lines = []
     for t, rs in by_test.items():
         cmp_ = [r for r in rs if r["kind"] != "momentum"]

@@ -53,7 +53,7 @@ def _upload_workload(w):
     return P, G, M
 
 
-FORMS = ("square", "direct")   # the default form of the NS step first
+FORMS = ("square", "direct", "folded")   # the default form of the NS step first
 
 
 def _run_and_check(w, samples, prop_groups=()):

@@ -399,7 +399,7 @@ def test_checkpoint_resume_bitwise(nsa):
 
 # ---- the two polynomial forms; per-parameter coefficient sets; eps, rms ----
 
-@pytest.mark.parametrize("form", ["direct", "square"])
+@pytest.mark.parametrize("form", ["direct", "square", "folded"])
 def test_poly_forms_ragged(nsa, form):
     # Both bf16 forms of the NS step against the oracle over the ragged
     # shapes (the square form, the default, completes the polynomial to a
