@@ -127,6 +127,12 @@ __device__ __forceinline__ void dma16(const void* g, const void* lds_dst) {
   asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, off"
                :: "s"(__builtin_amdgcn_readfirstlane(lds_addr(lds_dst))), "v"(g) : "memory", "m0");
 }
+// The same with the LDS byte address given as a uniform base plus an
+// offset (both scalar: m0 is formed by one scalar add).
+__device__ __forceinline__ void dma16_off(const void* g, unsigned base, unsigned off) {
+  asm volatile("s_add_u32 m0, %0, %1\n\tglobal_load_lds_dwordx4 %2, off"
+               :: "s"(base), "s"(off), "v"(g) : "memory", "m0");
+}
 
 // Workgroup barrier without the release/acquire fence of __syncthreads():
 // the fence would wait for every outstanding global->LDS load, including
@@ -210,6 +216,12 @@ __device__ __forceinline__ Geom geom(const GemmArgs& g, bool sym) {
 // Columns at or beyond `colmax` (the padded width of the output) are
 // computed from clamped loads and never stored. `lds`: the K-slab stages,
 // reused as the epilogue tile.
+//
+// Update without an epilogue operand or the fused apply (the "drain" form:
+// the four non-final steps of the square and folded forms) skips the
+// shared epilogue tile: each wave writes its own 128 x 128 block into its
+// own stage and stores it from there, with no workgroup barrier between
+// forming the block and storing it (see the drain epilogue below).
 template <int ROLE, bool WIDE>
 __device__ __forceinline__ void gemm_tile(const GemmArgs& g, int mat, int I, int J, Stages& lds,
                                           const Claim& cl, int& next) {
@@ -249,6 +261,7 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& g, int mat, int I, int
   // Wave's 128-row block (stage rows of P) and 128-column block (of Q).
   const int rb0 = WIDE ? 0 : (wave >> 1) * 128;
   const int cb0 = WIDE ? wave * 128 : (wave & 1) * 128;
+  const bool drain = ROLE == kUpdate && !g.ptab && !g.update_operand;
 
   // LDS fill of one K-slab in loads of 16 stage rows of 64 B (1 KiB); the
   // loads are dealt round-robin over the waves (wave w issues loads w,
@@ -260,6 +273,7 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& g, int mat, int I, int
   const int nk = K / BK;
   const int last = nk - 1;
   static_assert(PR % 64 == 0, "P rows take whole rounds of the four waves' loads");
+  const unsigned lds0 = __builtin_amdgcn_readfirstlane(lds_addr(&lds[0][0]));
   auto fill_one = [&](int kt, int q) {
     const int k0 = kt * BK;   // kt <= last
     const int rb = (q * 4 + wave) * 16;
@@ -280,7 +294,16 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& g, int mat, int I, int
       qr = qr < qlast ? qr : qlast;   // rows past the output width: any valid row
       src = Q + (size_t)(q0 + qr) * K + k0 + ((lane & 3) ^ kswz(r)) * 8;
     }
-    dma16(src, &lds[kt & (kStages - 1)][rb * BK]);
+    if constexpr (ROLE == kUpdate) {
+      // LDS: stage kt % 4, row block rb = 16 (4q + wave), as a uniform
+      // base (stage and wave) plus 4 KiB per q: m0 stays a scalar add in
+      // the Update loop, whose scalar registers are scarce.
+      const unsigned base = __builtin_amdgcn_readfirstlane(
+          lds0 + (unsigned)((kt & (kStages - 1)) * (kStageRows * BK * 2) + wave * (16 * BK * 2)));
+      dma16_off(src, base, (unsigned)(q * (64 * BK * 2)));
+    } else {
+      dma16(src, &lds[kt & (kStages - 1)][rb * BK]);
+    }
   };
 
   // Fragments of a 16-deep K step (MFMA operand layout: lane l holds 8
@@ -400,6 +423,12 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& g, int mat, int I, int
       mfma_step(0, [&](int i) {
         if (i < 8) read_one(kt, 1, i, rf[1], cf[1]);
       }, F0{});
+      if (drain) {
+        // Every wave's last LDS reads have completed: the drain epilogue
+        // may overwrite the stages.
+        __builtin_amdgcn_s_waitcnt(vmcnt_lgkm0(63));
+        lds_barrier();
+      }
       mfma_step(1, [](int) {}, F0{});
     }
   };
@@ -411,6 +440,70 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& g, int mat, int I, int
   slab(last - 1, std::integral_constant<int, 2>{}, std::false_type{});
   const int claim = claim_issue(cl, tid);
   slab(last, std::integral_constant<int, 3>{}, std::false_type{});
+
+  constexpr int kBatch = 8;
+  if constexpr (ROLE == kUpdate) {
+    if (drain) {
+      // Drain epilogue: each wave takes its 128 x 128 block through its own
+      // 32 x 128 strip of stage 3 (8 KiB), four strips in turn. After the
+      // barrier of the last slab no stage is read or filled; the next
+      // tile's prologue fills stages 0-2 only, and stage 3 is filled after
+      // that tile's first barrier, which every wave passes only after this
+      // epilogue. A strip's 16 accumulator quads are scaled (step 1),
+      // rounded to bf16 and written at (row, chunk ^ row % 16), read back
+      // as 4 rows x 16 chunks per instruction and stored as 256 B row runs.
+      // A wave's LDS accesses complete in issue order, so no wait separates
+      // a strip's writes from its reads or from the next strip's writes.
+      // (Measured: one strip at a time is faster than forming the whole
+      // block in a stage of its own before storing it.)
+      int etid = threadIdx.x;
+      asm volatile("" : "+v"(etid));
+      const int el = etid & 63, l32 = el & 31, hf = el >> 5;
+      const int rr = el >> 4, cc = el & 15;
+      bf16_t* const W = &lds[kStages - 1][0] + wave * (32 * 128);
+      bf16_t* const ob = static_cast<bf16_t*>(g.out) + (size_t)mat * g.mat_x +
+                         (size_t)(I * TILE + rb0) * g.n_pad + q0 + cb0;
+      // Wide tiles: a wave's 128 columns are all inside the padded width
+      // or all past it (both are multiples of 256 from q0).
+      const bool live = !WIDE || cb0 < colmax - q0;
+      const float sc = g.scales ? g.scales[mat] : 1.0f;
+      auto run_drain = [&](auto scaled) {
+        constexpr bool SC = decltype(scaled)::value;
+#pragma unroll
+        for (int b = 0; b < 4; ++b) {
+#pragma unroll
+          for (int a = 0; a < 4; ++a) {
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+              float v[4];
+#pragma unroll
+              for (int e = 0; e < 4; ++e) v[e] = SC ? acc[a][b][4 * q + e] * sc : acc[a][b][4 * q + e];
+              uint2 o;
+              o.x = f32x2_to_bf16x2(v[0], v[1]);
+              o.y = f32x2_to_bf16x2(v[2], v[3]);
+              *reinterpret_cast<uint2*>(W + l32 * 128 + (((4 * a + q) ^ (l32 & 15)) << 3) + 4 * hf) = o;
+            }
+          }
+          asm volatile("" ::: "memory");
+          uint4 v[8];
+#pragma unroll
+          for (int u = 0; u < 8; ++u) {
+            const int row = 4 * u + rr;
+            v[u] = *reinterpret_cast<const uint4*>(W + row * 128 + ((cc ^ (row & 15)) << 3));
+          }
+          keep_batch(v);
+          asm volatile("" ::: "memory");
+          if (live) {
+#pragma unroll
+            for (int u = 0; u < 8; ++u) store16_at(ob, (32 * b + 4 * u + rr) * g.n_pad + 8 * cc, v[u]);
+          }
+        }
+      };
+      if (g.scales) run_drain(std::true_type{});
+      else run_drain(std::false_type{});
+      return;
+    }
+  }
 
   // ---- epilogue ----------------------------------------------------------
   {
@@ -586,7 +679,6 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& g, int mat, int I, int
     }
     return __builtin_bit_cast(uint4, __builtin_shufflevector(h[0], h[1], 0, 1, 2, 3, 4, 5, 6, 7));
   };
-  constexpr int kBatch = 8;
   if constexpr (ROLE == kUpdate) {
     if (g.ptab) {
       // Last step with the apply fused: X' (rounded to bf16 in T, the same
@@ -960,6 +1052,30 @@ __device__ __forceinline__ void gemm_diag_tile(const GemmArgs& g, int mat, int I
   }
 }
 
+// Update tile u of a matrix: full tiles over all rows x columns (row-major,
+// or in groups of kGroupRows tile rows, column-major inside a group: the
+// tiles an XCD runs at once then form a block of about 4 x 8 tiles that
+// share 4 row panels of B' and 8 column panels of X; row-major, a wide X
+// would be streamed again for every tile row), then the wide tiles of the
+// half row (I = F, columns 2w*256 ..).
+__device__ __forceinline__ void update_coords(const Geom& G, int u, int& I, int& J, bool& wide) {
+  wide = u >= G.full;
+  if (wide) {
+    I = G.F;
+    J = 2 * (u - G.full);
+  } else if (G.tn <= kRowMajorMax) {
+    I = u / G.tn;
+    J = u % G.tn;
+  } else {
+    const int gsz = kGroupRows * G.tn;
+    const int r0 = (u / gsz) * kGroupRows;
+    const int gm = G.F - r0 < kGroupRows ? G.F - r0 : kGroupRows;
+    const int v = u - r0 * G.tn;
+    I = r0 + v % gm;
+    J = v / gm;
+  }
+}
+
 // One grid covers every tile of every computed matrix of the batch: at
 // most one workgroup per CU, a multiple of 8, each looping over the tiles
 // of its XCD's contiguous range, so each XCD's L2 serves whole matrices.
@@ -999,13 +1115,24 @@ void ns_gemm_bf16(GemmArgs g) {
     int next = 0;
     const int mat = g.live_list ? g.live_list[t / G.per_mat] : t / G.per_mat;
     const int u = t % G.per_mat;
+    if constexpr (ROLE == kUpdate) {
+      int I, J;
+      bool wide;
+      update_coords(G, u, I, J, wide);
+      if (wide) gemm_tile<ROLE, true>(g, mat, I, J, lds, cl, next);
+      else gemm_tile<ROLE, false>(g, mat, I, J, lds, cl, next);
+      // After a drain epilogue the next prologue needs no barrier (it
+      // fills stages 0-2; the drain used stage 3).
+      if (g.ptab || g.update_operand) __syncthreads();   // the epilogue's LDS reads are done before the next fills
+      t = sched ? __builtin_amdgcn_readfirstlane(next) : t + step;
+    } else {
     if (u < G.full) {
       int I, J;
-      if (kSym && G.F <= kRowMajorMax) {   // lower triangle, row-major: row I holds I + 1 tiles
+      if (G.F <= kRowMajorMax) {   // lower triangle, row-major: row I holds I + 1 tiles
         I = 0;
         while ((I + 1) * (I + 2) / 2 <= u) ++I;
         J = u - I * (I + 1) / 2;
-      } else if (kSym) {
+      } else {
         // Lower triangle in bands of kGroupRows tile rows, column-major
         // inside a band (the full columns J < r0, then the band's own
         // triangle), so the tiles an XCD runs at once share a few row and
@@ -1027,27 +1154,9 @@ void ns_gemm_bf16(GemmArgs g) {
           J = r0 + c;
           I = J + v;
         }
-      } else if (G.tn <= kRowMajorMax) {
-        I = u / G.tn;
-        J = u % G.tn;
-      } else {
-        // Groups of kGroupRows tile rows, column-major inside a group: the
-        // tiles an XCD runs at once form a block of about 4 x 8 tiles that
-        // share 4 row panels of B' and 8 column panels of X. (Row-major,
-        // a wide X would be streamed again for every tile row.)
-        const int gsz = kGroupRows * G.tn;
-        const int r0 = (u / gsz) * kGroupRows;
-        const int gm = G.F - r0 < kGroupRows ? G.F - r0 : kGroupRows;
-        const int v = u - r0 * G.tn;
-        I = r0 + v % gm;
-        J = v / gm;
       }
-      if constexpr (kSym) {
-        if (I == J && !(ROLE == kPoly && g.poly_operand)) gemm_diag_tile<ROLE>(g, mat, I, lds, cl, next);
-        else gemm_tile<ROLE, false>(g, mat, I, J, lds, cl, next);
-      } else {
-        gemm_tile<ROLE, false>(g, mat, I, J, lds, cl, next);
-      }
+      if (I == J && !(ROLE == kPoly && g.poly_operand)) gemm_diag_tile<ROLE>(g, mat, I, lds, cl, next);
+      else gemm_tile<ROLE, false>(g, mat, I, J, lds, cl, next);
     } else {
       gemm_tile<ROLE, true>(g, mat, G.F, 2 * (u - G.full), lds, cl, next);
     }
@@ -1056,6 +1165,7 @@ void ns_gemm_bf16(GemmArgs g) {
     // atomic, passed on through the workgroup's slot in global memory, as
     // the stages take all of the LDS).
     t = sched ? __builtin_amdgcn_readfirstlane(next) : t + step;
+    }
   }
   if (sched && threadIdx.x == 0) {
     // Every workgroup has claimed its last tile: the last one to get here
