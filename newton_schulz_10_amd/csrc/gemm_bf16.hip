@@ -48,11 +48,17 @@
 //  * The fill loads are interleaved with the MFMAs (one 1 KiB load after
 //    every 4 MFMAs): issued in a burst they back up the address unit and
 //    stall the wave's MFMA issue behind them.
-//  * Epilogue through LDS: the operand tile of Poly is loaded into LDS
-//    with coalesced direct loads, each wave forms its outputs in fp32
-//    and writes bf16 back in place, and the finished tile leaves LDS as
-//    coalesced 16 B row stores and, transposed, as the mirror
-//    tile (Gram/Poly) or the X'^T tile (Update).
+//  * Epilogues through LDS. Drain form (Update in the non-final steps, and
+//    Poly's off-diagonal tiles, when no epilogue reads an operand tile):
+//    after one barrier in the last K-slab each wave forms its 128 x 128
+//    block in fp32 and passes it through a private 32 x 128 strip of the
+//    fourth stage to coalesced row stores (and transposing gathers for
+//    the mirror), with no further workgroup barrier; the next tile's
+//    prologue fills the other three stages meanwhile. Shared form (Gram,
+//    diagonal and wide tiles, operand tiles, the fused apply): the whole
+//    tile is formed in LDS (an operand tile loaded there first with
+//    coalesced direct loads) and leaves it as 16 B row stores and,
+//    transposed, as the mirror tile or the parameter's rows.
 //  * One grid covers every tile of every matrix of the batch: one workgroup
 //    per CU looping over a contiguous (per XCD) range of tiles, so each
 //    XCD's L2 serves whole matrices (see ns_gemm_bf16 below).
@@ -111,6 +117,12 @@ __device__ __forceinline__ int xswz(int k) { return (k & 3) * 4; }
 // (the column gathers of the transposed store); whole-row reads touch
 // every chunk of one row once.
 __device__ __forceinline__ int eswz(int i) { return (i & 31) ^ ((i >> 5) & 7); }
+
+// Chunk swizzle of the drain epilogue's strips (32 rows of 16 chunks of
+// 16 B): a permutation of the row's low 4 bits, so rows 0-15 (and 16-31)
+// get 16 distinct chunks for the MFMA-layout writes, and a transposing
+// read's 16 rows (8 g + 4 h + j, g < 4, j < 4) hit each chunk pair twice.
+__device__ __forceinline__ int dswz(int r) { return ((r & 3) << 1) | ((r >> 2) & 1) | (r & 8); }
 
 // Direct global->LDS load: lane l's 16 bytes land at lds_dst + 16*l.
 // Issued as inline asm so that the compiler does not track it (its
@@ -261,7 +273,13 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& g, int mat, int I, int
   // Wave's 128-row block (stage rows of P) and 128-column block (of Q).
   const int rb0 = WIDE ? 0 : (wave >> 1) * 128;
   const int cb0 = WIDE ? wave * 128 : (wave & 1) * 128;
-  const bool drain = ROLE == kUpdate && !g.ptab && !g.update_operand;
+  // Drain epilogue (see below): Update without an epilogue operand or the
+  // fused apply; Poly full tiles off the diagonal without an operand tile.
+  // (Gram claims its tiles dynamically, which needs the broadcast barrier
+  // of the shared epilogue.)
+  const bool drain = (ROLE == kUpdate) ? (!g.ptab && !g.update_operand)
+                     : (ROLE == kPoly) ? (!WIDE && I != J && !g.poly_operand && !cl.ctr)
+                                       : false;
 
   // LDS fill of one K-slab in loads of 16 stage rows of 64 B (1 KiB); the
   // loads are dealt round-robin over the waves (wave w issues loads w,
@@ -442,67 +460,92 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& g, int mat, int I, int
   slab(last, std::integral_constant<int, 3>{}, std::false_type{});
 
   constexpr int kBatch = 8;
-  if constexpr (ROLE == kUpdate) {
-    if (drain) {
-      // Drain epilogue: each wave takes its 128 x 128 block through its own
-      // 32 x 128 strip of stage 3 (8 KiB), four strips in turn. After the
-      // barrier of the last slab no stage is read or filled; the next
-      // tile's prologue fills stages 0-2 only, and stage 3 is filled after
-      // that tile's first barrier, which every wave passes only after this
-      // epilogue. A strip's 16 accumulator quads are scaled (step 1),
-      // rounded to bf16 and written at (row, chunk ^ row % 16), read back
-      // as 4 rows x 16 chunks per instruction and stored as 256 B row runs.
-      // A wave's LDS accesses complete in issue order, so no wait separates
-      // a strip's writes from its reads or from the next strip's writes.
-      // (Measured: one strip at a time is faster than forming the whole
-      // block in a stage of its own before storing it.)
-      int etid = threadIdx.x;
-      asm volatile("" : "+v"(etid));
-      const int el = etid & 63, l32 = el & 31, hf = el >> 5;
-      const int rr = el >> 4, cc = el & 15;
-      bf16_t* const W = &lds[kStages - 1][0] + wave * (32 * 128);
-      bf16_t* const ob = static_cast<bf16_t*>(g.out) + (size_t)mat * g.mat_x +
-                         (size_t)(I * TILE + rb0) * g.n_pad + q0 + cb0;
-      // Wide tiles: a wave's 128 columns are all inside the padded width
-      // or all past it (both are multiples of 256 from q0).
-      const bool live = !WIDE || cb0 < colmax - q0;
-      const float sc = g.scales ? g.scales[mat] : 1.0f;
-      auto run_drain = [&](auto scaled) {
-        constexpr bool SC = decltype(scaled)::value;
+  if (drain) {
+    // Drain epilogue: each wave takes its 128 x 128 block through its own
+    // 32 x 128 strip of stage 3 (8 KiB), four strips in turn. After the
+    // barrier of the last slab no stage is read or filled; the next tile's
+    // prologue fills stages 0-2 only, and stage 3 is filled after that
+    // tile's first barrier, which every wave passes only after this
+    // epilogue. A strip's 16 accumulator quads are formed in fp32 (Update:
+    // times the first step's scale; Poly: times c), rounded to bf16 and
+    // written at (row, chunk ^ dswz(row)); read back as 4 rows x 16 chunks
+    // per instruction and stored as 256 B row runs; Poly also gathers the
+    // strip's columns with transposing reads and stores them as 64 B runs
+    // of the mirror tile. A wave's LDS accesses complete
+    // in issue order, so no wait separates a strip's writes from its reads
+    // or from the next strip's writes. (Measured on Update: one strip at a
+    // time is faster than forming the whole block in a stage of its own.)
+    int etid = threadIdx.x;
+    asm volatile("" : "+v"(etid));
+    const int el = etid & 63, l32 = el & 31, hf = el >> 5;
+    const int rr = el >> 4, cc = el & 15;
+    const int grp = el >> 4, jj = el & 15;
+    bf16_t* const W = &lds[kStages - 1][0] + wave * (32 * 128);
+    const int ld = (ROLE == kUpdate) ? g.n_pad : g.m_pad;
+    bf16_t* const obase = static_cast<bf16_t*>(g.out) + (size_t)mat * ((ROLE == kUpdate) ? g.mat_x : g.mat_a);
+    bf16_t* const ob = obase + (size_t)(I * TILE + rb0) * ld + q0 + cb0;
+    bf16_t* const ob2 = obase + (size_t)(q0 + cb0) * ld + I * TILE + rb0;   // mirror (Poly)
+    // Wide Update tiles: a wave's 128 columns are all inside the padded
+    // width or all past it (both are multiples of 256 from q0).
+    const bool live = !WIDE || cb0 < colmax - q0;
+    float sc = (ROLE == kPoly) ? g.cc : 1.0f;
+    if (ROLE == kUpdate && g.scales) sc = g.scales[mat];
+    auto run_drain = [&](auto scaled) {
+      constexpr bool SC = decltype(scaled)::value;
 #pragma unroll
-        for (int b = 0; b < 4; ++b) {
+      for (int b = 0; b < 4; ++b) {
 #pragma unroll
-          for (int a = 0; a < 4; ++a) {
+        for (int a = 0; a < 4; ++a) {
 #pragma unroll
-            for (int q = 0; q < 4; ++q) {
-              float v[4];
+          for (int q = 0; q < 4; ++q) {
+            float v[4];
 #pragma unroll
-              for (int e = 0; e < 4; ++e) v[e] = SC ? acc[a][b][4 * q + e] * sc : acc[a][b][4 * q + e];
-              uint2 o;
-              o.x = f32x2_to_bf16x2(v[0], v[1]);
-              o.y = f32x2_to_bf16x2(v[2], v[3]);
-              *reinterpret_cast<uint2*>(W + l32 * 128 + (((4 * a + q) ^ (l32 & 15)) << 3) + 4 * hf) = o;
-            }
-          }
-          asm volatile("" ::: "memory");
-          uint4 v[8];
-#pragma unroll
-          for (int u = 0; u < 8; ++u) {
-            const int row = 4 * u + rr;
-            v[u] = *reinterpret_cast<const uint4*>(W + row * 128 + ((cc ^ (row & 15)) << 3));
-          }
-          keep_batch(v);
-          asm volatile("" ::: "memory");
-          if (live) {
-#pragma unroll
-            for (int u = 0; u < 8; ++u) store16_at(ob, (32 * b + 4 * u + rr) * g.n_pad + 8 * cc, v[u]);
+            for (int e = 0; e < 4; ++e) v[e] = SC ? acc[a][b][4 * q + e] * sc : acc[a][b][4 * q + e];
+            uint2 o;
+            o.x = f32x2_to_bf16x2(v[0], v[1]);
+            o.y = f32x2_to_bf16x2(v[2], v[3]);
+            *reinterpret_cast<uint2*>(W + l32 * 128 + (((4 * a + q) ^ dswz(l32)) << 3) + 4 * hf) = o;
           }
         }
-      };
-      if (g.scales) run_drain(std::true_type{});
-      else run_drain(std::false_type{});
-      return;
-    }
+        asm volatile("" ::: "memory");
+        uint4 v[kBatch];
+#pragma unroll
+        for (int u = 0; u < kBatch; ++u) {
+          const int row = 4 * u + rr;
+          v[u] = *reinterpret_cast<const uint4*>(W + row * 128 + ((cc ^ dswz(row)) << 3));
+        }
+        keep_batch(v);
+        if (live) {
+#pragma unroll
+          for (int u = 0; u < kBatch; ++u) store16_at(ob, (32 * b + 4 * u + rr) * ld + 8 * cc, v[u]);
+        }
+        if constexpr (kSym) {
+          // Transposing gather: lane (grp, jj) receives column c0 + jj of
+          // strip rows 8 grp .. +7 (two ds_read_b64_tr_b16 of 4 rows each),
+          // 16 B of mirror row c0 + jj.
+#pragma unroll
+          for (int u = 0; u < kBatch; ++u) {
+            const int c0 = 16 * u;
+            s16x4 h[2];
+#pragma unroll
+            for (int half = 0; half < 2; ++half) {
+              const int row = 8 * grp + 4 * half + (jj >> 2);
+              const int col = c0 + 4 * (jj & 3);
+              h[half] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                  (lds_s16x4*)(W + row * 128 + ((((col >> 3) ^ dswz(row)) << 3) | (col & 7))));
+            }
+            v[u] = __builtin_bit_cast(uint4, __builtin_shufflevector(h[0], h[1], 0, 1, 2, 3, 4, 5, 6, 7));
+          }
+          keep_batch(v);
+#pragma unroll
+          for (int u = 0; u < kBatch; ++u) store16_at(ob2, (16 * u + jj) * ld + 32 * b + 8 * grp, v[u]);
+        }
+        asm volatile("" ::: "memory");
+      }
+    };
+    if (ROLE == kPoly || g.scales) run_drain(std::true_type{});
+    else run_drain(std::false_type{});
+    return;
   }
 
   // ---- epilogue ----------------------------------------------------------
@@ -1157,10 +1200,13 @@ void ns_gemm_bf16(GemmArgs g) {
       }
       if (I == J && !(ROLE == kPoly && g.poly_operand)) gemm_diag_tile<ROLE>(g, mat, I, lds, cl, next);
       else gemm_tile<ROLE, false>(g, mat, I, J, lds, cl, next);
+      // A drained tile (Poly, see gemm_tile) needs no barrier before the
+      // next fills.
+      if (ROLE == kGram || I == J || g.poly_operand || sched) __syncthreads();
     } else {
       gemm_tile<ROLE, true>(g, mat, G.F, 2 * (u - G.full), lds, cl, next);
+      __syncthreads();   // the epilogue's LDS reads are done before the next fills
     }
-    __syncthreads();   // the epilogue's LDS reads are done before the next fills
     // Dynamic schedule: the tile claimed during the epilogue (thread 0's
     // atomic, passed on through the workgroup's slot in global memory, as
     // the stages take all of the LDS).
