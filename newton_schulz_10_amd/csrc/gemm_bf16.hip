@@ -49,13 +49,14 @@
 //    every 4 MFMAs): issued in a burst they back up the address unit and
 //    stall the wave's MFMA issue behind them.
 //  * Epilogues through LDS. Drain form (Update in the non-final steps, and
-//    Poly's off-diagonal tiles, when no epilogue reads an operand tile):
+//    the off-diagonal tiles of Gram and Poly, when no epilogue reads an
+//    operand tile):
 //    after one barrier in the last K-slab each wave forms its 128 x 128
 //    block in fp32 and passes it through a private 32 x 128 strip of the
 //    fourth stage to coalesced row stores (and transposing gathers for
 //    the mirror), with no further workgroup barrier; the next tile's
-//    prologue fills the other three stages meanwhile. Shared form (Gram,
-//    diagonal and wide tiles, operand tiles, the fused apply): the whole
+//    prologue fills the other three stages meanwhile. Shared form
+//    (diagonal and wide tiles, operand tiles, the fused apply): the whole
 //    tile is formed in LDS (an operand tile loaded there first with
 //    coalesced direct loads) and leaves it as 16 B row stores and,
 //    transposed, as the mirror tile or the parameter's rows.
@@ -179,10 +180,11 @@ typedef bf16_t Stages[kStages][kStageRows * BK];
 // Dynamic tile claim of the persistent loop (see ns_gemm_bf16). Thread 0
 // claims the next tile (an atomic on the XCD's counter) when the last
 // K-slab of the current one starts: that slab issues no loads, so no wait
-// in it covers the atomic. The claim is published through the workgroup's
-// slot before the barrier that follows the fp32 epilogue form, read back by
-// every thread after it and first used when the tile is done, so neither
-// latency delays the tile.
+// in it covers the atomic. Shared epilogue: the claim is published through
+// the workgroup's slot in global memory before the barrier that follows
+// the fp32 epilogue form, read back by every thread after it and first
+// used when the tile is done, so neither latency delays the tile. Drain
+// epilogue: it passes through LDS (see gemm_tile).
 struct Claim {
   int* ctr;    // the XCD's tile counter, or nullptr (static schedule)
   int* slot;   // the workgroup's broadcast slot
@@ -194,12 +196,13 @@ __device__ __forceinline__ int claim_issue(const Claim& c, int tid) {
   if (c.ctr && tid == 0) v = atomicAdd(c.ctr, 1);
   return v;
 }
+// The tile a claim stands for; a claim past the range (or any value
+// outside it) ends the loop.
+__device__ __forceinline__ int claim_tile(const Claim& c, int claim) {
+  return (claim >= 0 && claim < c.end - c.first) ? c.first + claim : c.end;
+}
 __device__ __forceinline__ void claim_publish(const Claim& c, int tid, int claim) {
-  if (c.ctr && tid == 0) {
-    // A claim past the range (or any value outside it) ends the loop.
-    const int next = (claim >= 0 && claim < c.end - c.first) ? c.first + claim : c.end;
-    __hip_atomic_store(c.slot, next, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  }
+  if (c.ctr && tid == 0) __hip_atomic_store(c.slot, claim_tile(c, claim), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 __device__ __forceinline__ int claim_load(const Claim& c) {
   return c.ctr ? __hip_atomic_load(c.slot, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) : 0;
@@ -274,12 +277,10 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& g, int mat, int I, int
   const int rb0 = WIDE ? 0 : (wave >> 1) * 128;
   const int cb0 = WIDE ? wave * 128 : (wave & 1) * 128;
   // Drain epilogue (see below): Update without an epilogue operand or the
-  // fused apply; Poly full tiles off the diagonal without an operand tile.
-  // (Gram claims its tiles dynamically, which needs the broadcast barrier
-  // of the shared epilogue.)
+  // fused apply; Gram/Poly full tiles off the diagonal without an operand
+  // tile.
   const bool drain = (ROLE == kUpdate) ? (!g.ptab && !g.update_operand)
-                     : (ROLE == kPoly) ? (!WIDE && I != J && !g.poly_operand && !cl.ctr)
-                                       : false;
+                                       : (!WIDE && I != J && !(ROLE == kPoly && g.poly_operand));
 
   // LDS fill of one K-slab in loads of 16 stage rows of 64 B (1 KiB); the
   // loads are dealt round-robin over the waves (wave w issues loads w,
@@ -466,12 +467,16 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& g, int mat, int I, int
     // barrier of the last slab no stage is read or filled; the next tile's
     // prologue fills stages 0-2 only, and stage 3 is filled after that
     // tile's first barrier, which every wave passes only after this
-    // epilogue. A strip's 16 accumulator quads are formed in fp32 (Update:
-    // times the first step's scale; Poly: times c), rounded to bf16 and
-    // written at (row, chunk ^ dswz(row)); read back as 4 rows x 16 chunks
-    // per instruction and stored as 256 B row runs; Poly also gathers the
-    // strip's columns with transposing reads and stores them as 64 B runs
-    // of the mirror tile. A wave's LDS accesses complete
+    // epilogue. A strip's 16 accumulator quads are formed in fp32 (Update
+    // and Gram: times the first step's scale, s resp. s^2; Poly: times c),
+    // rounded to bf16 and written at (row, chunk ^ dswz(row)); read back as
+    // 4 rows x 16 chunks per instruction and stored as 256 B row runs;
+    // Gram/Poly also gather the strip's columns with transposing reads and
+    // store them as 64 B runs of the mirror tile. With dynamic claims
+    // (Gram), thread 0 puts the claimed tile in stage 3 past the strips
+    // (row 512 on: no full tile's fill reaches it, and stage 3 is next
+    // filled after the next tile's first barrier) after the second strip,
+    // and every thread reads it after a barrier there. A wave's LDS accesses complete
     // in issue order, so no wait separates a strip's writes from its reads
     // or from the next strip's writes. (Measured on Update: one strip at a
     // time is faster than forming the whole block in a stage of its own.)
@@ -484,12 +489,15 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& g, int mat, int I, int
     const int ld = (ROLE == kUpdate) ? g.n_pad : g.m_pad;
     bf16_t* const obase = static_cast<bf16_t*>(g.out) + (size_t)mat * ((ROLE == kUpdate) ? g.mat_x : g.mat_a);
     bf16_t* const ob = obase + (size_t)(I * TILE + rb0) * ld + q0 + cb0;
-    bf16_t* const ob2 = obase + (size_t)(q0 + cb0) * ld + I * TILE + rb0;   // mirror (Poly)
+    bf16_t* const ob2 = obase + (size_t)(q0 + cb0) * ld + I * TILE + rb0;   // mirror (Gram/Poly)
     // Wide Update tiles: a wave's 128 columns are all inside the padded
     // width or all past it (both are multiples of 256 from q0).
     const bool live = !WIDE || cb0 < colmax - q0;
     float sc = (ROLE == kPoly) ? g.cc : 1.0f;
-    if (ROLE == kUpdate && g.scales) sc = g.scales[mat];
+    if (ROLE != kPoly && g.scales) {
+      const float sv = g.scales[mat];
+      sc = (ROLE == kGram) ? sv * sv : sv;
+    }
     auto run_drain = [&](auto scaled) {
       constexpr bool SC = decltype(scaled)::value;
 #pragma unroll
@@ -541,6 +549,13 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& g, int mat, int I, int
           for (int u = 0; u < kBatch; ++u) store16_at(ob2, (16 * u + jj) * ld + 32 * b + 8 * grp, v[u]);
         }
         asm volatile("" ::: "memory");
+        if (ROLE == kGram && b == 1 && cl.ctr) {
+          int* const slot = reinterpret_cast<int*>(&lds[kStages - 1][512 * BK]);
+          if (etid == 0) *slot = claim_tile(cl, claim);
+          __builtin_amdgcn_s_waitcnt(vmcnt_lgkm0(63));
+          lds_barrier();
+          next = *slot;
+        }
       }
     };
     if (ROLE == kPoly || g.scales) run_drain(std::true_type{});
@@ -1200,9 +1215,9 @@ void ns_gemm_bf16(GemmArgs g) {
       }
       if (I == J && !(ROLE == kPoly && g.poly_operand)) gemm_diag_tile<ROLE>(g, mat, I, lds, cl, next);
       else gemm_tile<ROLE, false>(g, mat, I, J, lds, cl, next);
-      // A drained tile (Poly, see gemm_tile) needs no barrier before the
-      // next fills.
-      if (ROLE == kGram || I == J || g.poly_operand || sched) __syncthreads();
+      // A drained tile (see gemm_tile) needs no barrier before the next
+      // fills.
+      if (I == J || (ROLE == kPoly && g.poly_operand)) __syncthreads();
     } else {
       gemm_tile<ROLE, true>(g, mat, G.F, 2 * (u - G.full), lds, cl, next);
       __syncthreads();   // the epilogue's LDS reads are done before the next fills
