@@ -412,6 +412,32 @@ def test_poly_forms_ragged(nsa, form):
     _print(form, "form ragged worst rel err", worst)
 
 
+@pytest.mark.parametrize("form", ["square", "folded", "direct"])
+def test_drain_epilogue_edges(nsa, form):
+    # Shapes whose tiles reach the edges of the per-wave (drain) epilogues:
+    # 1408 x 1280 has m_pad = 5 * 256 + 128 (wide 128 x 512 tiles in
+    # every role) and an odd number of 256-column tiles, so the last wide
+    # Update tile has two waves past the padded width; both orientations;
+    # 24 + 8 matrices give more Update, Gram and Poly tiles than
+    # workgroups, so workgroups go on from a drained tile to the next (full,
+    # diagonal or wide). Sampled matrices against the oracle, all finite.
+    import torch
+    shapes = [(1408, 1280)] * 12 + [(1280, 1408)] * 12 + [(640, 896)] * 4 + [(896, 640)] * 4
+    case = workloads.random_case(41, shapes, "bf16", params_init="zero")
+    P, G, M = upload_case(case, "bf16")
+    nsa.muon_step(list(zip(P, G, M)), 0.02, 0.95, 5, poly_form=form)
+    torch.cuda.synchronize()
+    assert all(bool(torch.isfinite(p.float()).all()) for p in P)
+    for i in (0, 11, 12, 23, 24, 31):
+        c = case[i]
+        rp, rb, _ = oracle.muon_matrix_step(c["params"].as_f64(), c["grad"].as_f64(),
+                                            c["momentum"].astype(np.float64), 0.02, 0.95, 5)
+        e = check_update(c["params"].as_f64(), from_device(P[i]), rp, "bf16", BF16_TOL,
+                         label=f"{form} #{i} {shapes[i][0]}x{shapes[i][1]}")
+        assert e <= BF16_TOL, (form, i, e)
+        assert check_momentum(from_device(M[i]), rb, label=f"#{i}") <= MOM_TOL
+
+
 def test_per_parameter_coefficient_sets(nsa):
     # HyperParallel-FSDP section 6.2: per-parameter coefficient sets. Three
     # sets over matrices of two shapes, with same-shaped matrices on
