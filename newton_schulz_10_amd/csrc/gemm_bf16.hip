@@ -278,7 +278,9 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& g, int mat, int I, int
   const int cb0 = WIDE ? wave * 128 : (wave & 1) * 128;
   // Drain epilogue (see below): Update without an epilogue operand or the
   // fused apply; Gram/Poly full tiles off the diagonal without an operand
-  // tile.
+  // tile. (An operand tile loaded strip by strip in the drain leaves its
+  // load latency exposed on every strip: measured far slower than loading
+  // it whole into the shared epilogue tile.)
   const bool drain = (ROLE == kUpdate) ? (!g.ptab && !g.update_operand)
                                        : (!WIDE && I != J && !(ROLE == kPoly && g.poly_operand));
 
@@ -476,10 +478,11 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& g, int mat, int I, int
     // (Gram), thread 0 puts the claimed tile in stage 3 past the strips
     // (row 512 on: no full tile's fill reaches it, and stage 3 is next
     // filled after the next tile's first barrier) after the second strip,
-    // and every thread reads it after a barrier there. A wave's LDS accesses complete
-    // in issue order, so no wait separates a strip's writes from its reads
-    // or from the next strip's writes. (Measured on Update: one strip at a
-    // time is faster than forming the whole block in a stage of its own.)
+    // and every thread reads it after a barrier there. A wave's LDS
+    // accesses complete in issue order, so no wait
+    // separates a strip's writes from its reads or from the next strip's
+    // writes. (Measured on Update: one strip at a time is faster than
+    // forming the whole block in a stage of its own.)
     int etid = threadIdx.x;
     asm volatile("" : "+v"(etid));
     const int el = etid & 63, l32 = el & 31, hf = el >> 5;
@@ -868,8 +871,8 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& g, int mat, int I, int
   }
 }
 
-// Diagonal tile of A'/B' (I == J, full, no epilogue operand). The block is
-// symmetric and its P and Q rows are the same 256 rows, so those are staged
+// Diagonal tile of A'/B' (I == J, full). The block is symmetric and its P
+// and Q rows are the same 256 rows, so those are staged
 // once, and only the 36 of its 64 blocks of 32 x 32 on or below the
 // diagonal are multiplied:
 //   waves 0 and 3: the lower triangles of the two diagonal quadrants (rows
@@ -878,6 +881,8 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& g, int mat, int I, int
 // The 28 blocks above the diagonal are the transposes of blocks below it,
 // element for element as the products are (the MFMA multiplies exactly
 // and sums in the same k order), copied in LDS before the tile is stored.
+// With Poly's operand tile (b A + c A A, A exactly symmetric as stored) the
+// formed blocks stay exact transposes of each other.
 // Kind 0 (triangle): MFMA i of a step multiplies column fragment
 // diag_a(0, i) by row fragment diag_b(0, i), over the pairs b >= a; kind 1
 // (rectangle): 2 column x 4 row fragments.
@@ -1004,8 +1009,23 @@ __device__ __forceinline__ void gemm_diag_tile(const GemmArgs& g, int mat, int I
     __builtin_amdgcn_s_waitcnt(0x0070);  // vmcnt(0) lgkmcnt(0): stages no longer read
     lds_barrier();
 
+    if (ROLE == kPoly && g.poly_operand) {
+      // Operand tile A(I, I) into T (as in gemm_tile: 128 loads of 1 KiB,
+      // 32 per wave, chunk (l % 32) ^ eswz(row) of the row).
+      const bf16_t* E = P;   // rows I*256 .. of A; the tile starts at column I*256
+#pragma unroll 8
+      for (int q = 0; q < 32; ++q) {
+        const int i0 = (wave * 32 + q) * 2;
+        const int i = i0 + (lane >> 5);
+        dma16(E + (size_t)i * K + I * TILE + ((lane & 31) ^ eswz(i)) * 8, T + i0 * QR);
+      }
+      __builtin_amdgcn_s_waitcnt(vmcnt(0));
+      lds_barrier();
+    }
+
     // fp32 form, rounded once to bf16 into T (rows of 256, chunks swizzled
-    // by eswz): Gram A' = sc * acc + d I, Poly B' = c acc + d I. acc[a][b]
+    // by eswz): Gram A' = sc * acc + d I, Poly B' = c acc + d I, or with
+    // the operand tile (in T at the same place) B' = b A + c acc + d I. acc[a][b]
     // element v: row rbase + 32b + lane%32, columns cbase + 32a + 8*(v/4) +
     // 4*(lane/32) + v%4; on a block with a == b of kind 0 the diagonal is
     // element 4*(l/8) + l%4 (l = lane % 32) of the lanes with lane/32 ==
@@ -1014,28 +1034,47 @@ __device__ __forceinline__ void gemm_diag_tile(const GemmArgs& g, int mat, int I
     asm volatile("" : "+v"(etid));
     const int el = etid & 63, l32 = el & 31;
     const int dsel = (KIND == 0 && (el >> 5) == ((l32 >> 2) & 1)) ? 4 * (l32 >> 3) + (l32 & 3) : -1;
+    auto form = [&](auto opnd) {
+      constexpr bool OP = decltype(opnd)::value;
 #pragma unroll
-    for (int i = 0; i < NM; ++i) {
-      const int a = diag_a(KIND, i), b = diag_b(KIND, i);
-      const int row_i = rbase + b * 32 + l32;
-      bf16_t* row = T + row_i * QR;
-      const int sw = eswz(row_i);
+      for (int i = 0; i < NM; ++i) {
+        const int a = diag_a(KIND, i), b = diag_b(KIND, i);
+        const int row_i = rbase + b * 32 + l32;
+        bf16_t* row = T + row_i * QR;
+        const int sw = eswz(row_i);
+        auto at = [&](int q) {
+          const int j = cbase + a * 32 + 8 * q + 4 * (el >> 5);
+          return reinterpret_cast<uint2*>(row + (((j >> 3) ^ sw) << 3) + (j & 7));
+        };
+        // Operand reads of the block ahead of its writes (in place).
+        uint2 w[4] = {};
+        if (OP) {
 #pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        float v[4];
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          v[e] = acc[a][b][4 * q + e];
-          v[e] = (ROLE == kPoly) ? v[e] * g.cc : v[e] * sc;
-          if (KIND == 0 && a == b && dgon) v[e] += (4 * q + e == dsel) ? g.diag_add : 0.0f;
+          for (int q = 0; q < 4; ++q) w[q] = *at(q);
         }
-        const int j = cbase + a * 32 + 8 * q + 4 * (el >> 5);
-        uint2 o;
-        o.x = f32x2_to_bf16x2(v[0], v[1]);
-        o.y = f32x2_to_bf16x2(v[2], v[3]);
-        *reinterpret_cast<uint2*>(row + (((j >> 3) ^ sw) << 3) + (j & 7)) = o;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          float v[4];
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            v[e] = acc[a][b][4 * q + e];
+            if (OP) {
+              const unsigned h = (e < 2 ? w[q].x : w[q].y) >> (16 * (e & 1));
+              v[e] = fmaf(g.cb, bf16_to_f32(h & 0xffffu), g.cc * v[e]);
+            } else {
+              v[e] = (ROLE == kPoly) ? v[e] * g.cc : v[e] * sc;
+            }
+            if (KIND == 0 && a == b && dgon) v[e] += (4 * q + e == dsel) ? g.diag_add : 0.0f;
+          }
+          uint2 o;
+          o.x = f32x2_to_bf16x2(v[0], v[1]);
+          o.y = f32x2_to_bf16x2(v[2], v[3]);
+          *at(q) = o;
+        }
       }
-    }
+    };
+    if (ROLE == kPoly && g.poly_operand) form(std::true_type{});
+    else form(std::false_type{});
   };
   if (wave == 0 || wave == 3) {
     const int qb = wave == 0 ? 0 : 128;
@@ -1213,7 +1252,7 @@ void ns_gemm_bf16(GemmArgs g) {
           I = J + v;
         }
       }
-      if (I == J && !(ROLE == kPoly && g.poly_operand)) gemm_diag_tile<ROLE>(g, mat, I, lds, cl, next);
+      if (I == J) gemm_diag_tile<ROLE>(g, mat, I, lds, cl, next);
       else gemm_tile<ROLE, false>(g, mat, I, J, lds, cl, next);
       // A drained tile (see gemm_tile) needs no barrier before the next
       // fills.
