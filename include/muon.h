@@ -98,16 +98,17 @@ enum {
  *     and Update B' X, so no epilogue reads an operand tile. The diagonal of
  *     A + beta I and of B' is rounded to bf16 after the constants are added,
  *     which costs accuracy: measured relative Frobenius error of the update
- *     1.0-1.6e-2 on the workload shapes, against 0.8-1.3e-2 for the direct
- *     form (both within 2e-2).
+ *     1.0-1.6e-2 on the workload shapes (within 2e-2). The fastest form.
  *   MUON_POLY_DIRECT: the step as section 6.6 states it -- A = X X^T, B = b A
  *     + c A A (b A added in fp32 from the A tile in the epilogue), X' = a X +
  *     B X (a X added in fp32 from the X tile in the epilogue); A, B and X'
- *     are each rounded once. About 7% slower on 1408 x 2048 matrices.
+ *     are each rounded once. Error 0.86-1.26e-2; about 6% slower on the
+ *     1408 x 2048 expert bank.
  *   MUON_POLY_FOLDED: A = X X^T exact (no shift), B' = a I + b A + c A A
  *     formed in fp32 from the A tile in Poly's epilogue and rounded once,
  *     X' = B' X with no operand tile: the a X term rides in B' as in the
- *     square form, but A's diagonal keeps its bits.
+ *     square form, but A's diagonal keeps its bits. The most accurate
+ *     (0.78-0.95e-2); about 1.4% slower than the square form there.
  * The float32 path always computes the direct form. */
 enum { MUON_POLY_DIRECT = 0, MUON_POLY_SQUARE = 1, MUON_POLY_FOLDED = 2 };
 
