@@ -70,6 +70,9 @@ def parse():
     ap.add_argument("--mfma", metavar="MFMA_DIR",
                     help="with --summarize: a --pmc MfmaFlopsBF16 MfmaUtil run, for executed MFMA flops "
                          "and MFMA busy time per kernel")
+    ap.add_argument("--f32-ns", metavar="COUNTxMxN",
+                    help="side measurement instead of the step: muon_orthogonalize on COUNT float32 "
+                         "M x N matrices (the float32 NS path), nominal and executed TFLOP/s")
     ap.add_argument("--clock", metavar="CLOCK_DIR",
                     help="with --summarize: a --pmc GRBM_GUI_ACTIVE --kernel-trace run, for each kernel's "
                          "effective shader clock (GPU-busy cycles over the dispatch's duration)")
@@ -98,9 +101,9 @@ def executed_mfma_flops(rows: int, cols: int, ns_steps: int, poly_form: str = "s
     kind, from their tile geometry: m padded to 128 and n to 256 (m <= n);
     256 x 256 tiles, plus 128 x 512 tiles over the half tile row when m_pad
     is an odd multiple of 128; Gram and Poly over the lower triangle of
-    tiles, diagonal tiles multiplying 36 of their 64 blocks of 32 x 32
-    (Poly's only when no epilogue reads an operand tile, i.e. the square
-    form); Update over every tile of X'."""
+    tiles, diagonal tiles multiplying 36 of their 64 blocks of 32 x 32 (in
+    every form); Update over every tile of X'. The form does not change
+    the MFMA work (poly_form is kept for callers)."""
     m, n = min(rows, cols), max(rows, cols)
     mp, np_ = -(-m // 128) * 128, -(-n // 256) * 256
     F, half = mp // 256, mp % 256 != 0
@@ -114,7 +117,7 @@ def executed_mfma_flops(rows: int, cols: int, ns_steps: int, poly_form: str = "s
         return (F * (F - 1) // 2 * full_tile + F * diag_frac * full_tile + wide_sym * wide_tile) * K
 
     gram = sym(np_, 36 / 64)
-    poly = sym(mp, 36 / 64 if poly_form == "square" else 1.0)   # an epilogue operand takes the full tile
+    poly = sym(mp, 36 / 64)
     upd = (F * tu * full_tile + wide_upd * wide_tile) * mp
     return {"ns_gram": ns_steps * gram, "ns_poly": ns_steps * poly, "ns_update": ns_steps * upd}
 
@@ -494,6 +497,43 @@ def cpu_baseline(w, budget_s):
                       f"fp64 numpy, {el:.1f} s"}
 
 
+def f32_executed_flops(m: int, n: int, ns_steps: int) -> float:
+    """MFMA flops the float32 kernels execute per matrix: 64 x 64 tiles over
+    the padded shape, Gram and Poly on the upper tiles (diagonal tiles
+    whole)."""
+    mp, np_ = -(-m // 64) * 64, -(-n // 64) * 64
+    t = mp // 64
+    sym = t * (t + 1) // 2 * 64 * 64
+    return ns_steps * (2.0 * sym * np_ + 2.0 * sym * mp + 2.0 * mp * mp * np_)
+
+
+def f32_ns(args, torch, nsa) -> None:
+    """The float32 NS path (muon_orthogonalize) on synthetic N(0, 1)
+    matrices: one JSON line. A side figure, not the step's metric."""
+    cnt, m, n = (int(v) for v in args.f32_ns.lower().split("x"))
+    gen = torch.Generator(device="cuda").manual_seed(0)
+    X = [torch.randn(m, n, device="cuda", generator=gen) for _ in range(cnt)]
+    O = [torch.empty_like(x) for x in X]
+    for _ in range(args.warmup):
+        nsa.muon_orthogonalize(X, O)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(args.steps):
+        nsa.muon_orthogonalize(X, O)
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / args.steps
+    lo, hi = min(m, n), max(m, n)
+    nominal = cnt * float(nominal_ns_flops(lo, hi, 5))
+    executed = cnt * f32_executed_flops(lo, hi, 5)
+    print(json.dumps({"metric": "float32 NS TFLOP/s (muon_orthogonalize)", "value": nominal / ms / 1e9,
+                      "unit": "TFLOP/s", "executed_tflops": executed / ms / 1e9,
+                      "frac_of_fp32_peak_executed": executed / ms / 1e9 / 157.3, "ms_per_call": ms,
+                      "config": {"workload": f"{cnt} x {m}x{n} float32", "ns_steps": 5},
+                      "steps": args.steps, "warmup": args.warmup, "dtype": "f32", "data": "synthetic"}))
+
+
 def main():
     args = parse()
     if args.summarize:
@@ -508,6 +548,9 @@ def main():
     import workloads
 
     nsa.load()
+    if args.f32_ns:
+        f32_ns(args, torch, nsa)
+        return
     w = workloads.WORKLOADS[args.workload]
     banks = make_inputs(w)
     mats_per_step = w.num_matrices

@@ -1,13 +1,17 @@
 // Batched fp32 GEMMs of the quintic Newton-Schulz iteration (float32 path).
 //
-// Same three roles and epilogues as the bf16 path (see gemm_bf16.hip):
+// Same three roles and epilogues as the bf16 path (see gemm_bf16.hip), in
+// the direct form:
 //   Gram   : A  = sc * X X^T        (upper tiles, mirrored)
 //   Poly   : B  = b*A + c*(A A)     (A symmetric; upper tiles, mirrored)
 //   Update : X' = sc * (a*X + B X)
-// computed with fp32 FMA on the vector ALUs: 64x64 output tiles, 256
-// threads with 4x4 outputs each, K-slabs of 16 staged in LDS (K-major so
-// that the inner product reads are broadcasts / contiguous). The float32
-// path serves small groups where bf16 is not wanted; it is not tuned.
+// on the fp32 matrix cores (v_mfma_f32_32x32x2_f32): 64 x 64 output tiles,
+// 256 threads = 4 waves of 32 x 32 (one MFMA block of 16 fp32 accumulators
+// per lane). K-slabs of 16 staged K-major in LDS ([k][row]: a fragment
+// read is 32 consecutive floats per half-wave), double buffered: the next
+// slab's global loads are in flight while the current one is multiplied,
+// one barrier per slab. Small tiles and registers keep several workgroups
+// on a CU, which hide the load latency.
 #include "device_common.h"
 #include "kernels.h"
 
@@ -15,7 +19,8 @@ namespace muon {
 
 namespace {
 
-constexpr int TM = 64, TK = 16;
+constexpr int TM = 64, TK = 16, TP = TM + 4;   // tile edge, K-slab, padded LDS row
+typedef __attribute__((ext_vector_type(16))) float f32x16;
 
 __device__ __forceinline__ void upper_tile(int t, int nt, int& I, int& J) {
   int i = 0, rowlen = nt;
@@ -25,8 +30,8 @@ __device__ __forceinline__ void upper_tile(int t, int nt, int& I, int& J) {
 
 template <int ROLE>
 __global__ __launch_bounds__(256) void ns_gemm_f32(GemmArgs g) {
-  __shared__ float As[TK][TM + 4];
-  __shared__ float Bs[TK][TM + 4];
+  __shared__ __attribute__((aligned(16))) float As[2][TK][TP];
+  __shared__ __attribute__((aligned(16))) float Bs[2][TK][TP];   // rows of 272 B: float4 stores stay aligned
   constexpr bool kSym = (ROLE != kUpdate);
   const int tiles_m = g.m_pad / TM;
   const int tiles_n = kSym ? tiles_m : g.n_pad / TM;
@@ -54,47 +59,55 @@ __global__ __launch_bounds__(256) void ns_gemm_f32(GemmArgs g) {
   if (ROLE == kUpdate) Bop += (size_t)J * TM;
   else Bop += (size_t)(J * TM) * ldb;
 
-  const int tid = threadIdx.x, tx = tid & 15, ty = tid >> 4;
-  float acc[4][4];
-#pragma unroll
-  for (int r = 0; r < 4; ++r)
-#pragma unroll
-    for (int c = 0; c < 4; ++c) acc[r][c] = 0.0f;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int r0 = (wave >> 1) * 32, c0 = (wave & 1) * 32;   // the wave's 32 x 32 block
+  // Slab loads (one float4 of A and one of B per thread): A rows (and the
+  // rows of Q for Gram/Poly) as 16 k of a row; Update's B as 64 columns of
+  // one of 16 k rows of X.
+  const int lrow = tid >> 2, lkq = (tid & 3) * 4;
+  const int bkr = tid >> 4, bjq = (tid & 15) * 4;
+  float4 ra, rb;
+  auto load = [&](int k0) {
+    ra = *reinterpret_cast<const float4*>(Aop + (size_t)lrow * lda + k0 + lkq);
+    if (ROLE == kUpdate) rb = *reinterpret_cast<const float4*>(Bop + (size_t)(k0 + bkr) * ldb + bjq);
+    else rb = *reinterpret_cast<const float4*>(Bop + (size_t)lrow * ldb + k0 + lkq);
+  };
+  auto stash = [&](int buf) {
+    As[buf][lkq + 0][lrow] = ra.x; As[buf][lkq + 1][lrow] = ra.y;
+    As[buf][lkq + 2][lrow] = ra.z; As[buf][lkq + 3][lrow] = ra.w;
+    if (ROLE == kUpdate) {
+      *reinterpret_cast<float4*>(&Bs[buf][bkr][bjq]) = rb;
+    } else {
+      Bs[buf][lkq + 0][lrow] = rb.x; Bs[buf][lkq + 1][lrow] = rb.y;
+      Bs[buf][lkq + 2][lrow] = rb.z; Bs[buf][lkq + 3][lrow] = rb.w;
+    }
+  };
 
-  for (int k0 = 0; k0 < K; k0 += TK) {
-    {
-      const int row = tid >> 2, kq = (tid & 3) * 4;
-      const float4 va = *reinterpret_cast<const float4*>(Aop + (size_t)row * lda + k0 + kq);
-      As[kq + 0][row] = va.x; As[kq + 1][row] = va.y; As[kq + 2][row] = va.z; As[kq + 3][row] = va.w;
-      if (ROLE == kUpdate) {
-        const int kr = tid >> 4, jq = (tid & 15) * 4;
-        const float4 vb = *reinterpret_cast<const float4*>(Bop + (size_t)(k0 + kr) * ldb + jq);
-        Bs[kr][jq + 0] = vb.x; Bs[kr][jq + 1] = vb.y; Bs[kr][jq + 2] = vb.z; Bs[kr][jq + 3] = vb.w;
-      } else {
-        const float4 vb = *reinterpret_cast<const float4*>(Bop + (size_t)row * ldb + k0 + kq);
-        Bs[kq + 0][row] = vb.x; Bs[kq + 1][row] = vb.y; Bs[kq + 2][row] = vb.z; Bs[kq + 3][row] = vb.w;
-      }
+  // MFMA operands: lane l supplies A[r0 + l%32][k + l/32] and
+  // B[k + l/32][c0 + l%32]; accumulator element v of lane l is output
+  // (r0 + 8*(v/4) + 4*(l/32) + v%4, c0 + l%32).
+  f32x16 acc = {};
+  const int nk = K / TK;
+  load(0);
+  stash(0);
+  __syncthreads();
+  for (int s = 0; s < nk; ++s) {
+    const int buf = s & 1;
+    if (s + 1 < nk) load((s + 1) * TK);
+#pragma unroll
+    for (int kk = 0; kk < TK; kk += 2) {
+      const float av = As[buf][kk + (lane >> 5)][r0 + (lane & 31)];
+      const float bv = Bs[buf][kk + (lane >> 5)][c0 + (lane & 31)];
+      acc = __builtin_amdgcn_mfma_f32_32x32x2f32(av, bv, acc, 0, 0, 0);
     }
-    __syncthreads();
-#pragma unroll
-    for (int k = 0; k < TK; ++k) {
-      float av[4], bv[4];
-#pragma unroll
-      for (int r = 0; r < 4; ++r) av[r] = As[k][ty + 16 * r];
-#pragma unroll
-      for (int c = 0; c < 4; ++c) bv[c] = Bs[k][tx + 16 * c];
-#pragma unroll
-      for (int r = 0; r < 4; ++r)
-#pragma unroll
-        for (int c = 0; c < 4; ++c) acc[r][c] = fmaf(av[r], bv[c], acc[r][c]);
-    }
+    if (s + 1 < nk) stash(buf ^ 1);
     __syncthreads();
   }
 
   float sc = 1.0f;
   if (g.scales) {
-    const float s = g.scales[mat];
-    sc = (ROLE == kGram) ? s * s : s;
+    const float sv = g.scales[mat];
+    sc = (ROLE == kGram) ? sv * sv : sv;
   }
   float* out = static_cast<float*>(g.out);
   const int ldc = (ROLE == kUpdate) ? g.n_pad : g.m_pad;
@@ -102,22 +115,21 @@ __global__ __launch_bounds__(256) void ns_gemm_f32(GemmArgs g) {
   const float* ep = nullptr;
   if (ROLE == kPoly) ep = static_cast<const float*>(g.a) + (size_t)mat * g.mat_a;
   if (ROLE == kUpdate) ep = static_cast<const float*>(g.x) + (size_t)mat * g.mat_x;
+  const int gj = J * TM + c0 + (lane & 31);
 #pragma unroll
-  for (int r = 0; r < 4; ++r)
-#pragma unroll
-    for (int c = 0; c < 4; ++c) {
-      const int gi = I * TM + ty + 16 * r, gj = J * TM + tx + 16 * c;
-      const float a = acc[r][c];
-      float val;
-      if (ROLE == kGram) val = sc * a;
-      else if (ROLE == kPoly) val = fmaf(g.cb, ep[(size_t)gi * ldc + gj], g.cc * a);
-      else val = sc * fmaf(g.ca, ep[(size_t)gi * ldc + gj], a);
-      if (kSym) {
-        if (gi <= gj) { out[(size_t)gi * ldc + gj] = val; out[(size_t)gj * ldc + gi] = val; }
-      } else {
-        out[(size_t)gi * ldc + gj] = val;
-      }
+  for (int v = 0; v < 16; ++v) {
+    const int gi = I * TM + r0 + 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3);
+    const float a = acc[v];
+    float val;
+    if (ROLE == kGram) val = sc * a;
+    else if (ROLE == kPoly) val = fmaf(g.cb, ep[(size_t)gi * ldc + gj], g.cc * a);
+    else val = sc * fmaf(g.ca, ep[(size_t)gi * ldc + gj], a);
+    if (kSym) {
+      if (gi <= gj) { out[(size_t)gi * ldc + gj] = val; out[(size_t)gj * ldc + gi] = val; }
+    } else {
+      out[(size_t)gi * ldc + gj] = val;
     }
+  }
 }
 
 }  // namespace

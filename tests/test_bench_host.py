@@ -119,4 +119,15 @@ def test_executed_mfma_flops_model():
     assert e["ns_update"] == (5 * 8 * full + 4 * wide) * 1408
     assert e["ns_gram"] == pytest.approx((10 * full + 5 * 36 / 64 * full + 3 * wide) * 2048)
     assert bench.executed_mfma_flops(2048, 1408, 1) == e
-    assert bench.executed_mfma_flops(1408, 2048, 1, "direct")["ns_poly"] == (15 * full + 3 * wide) * 1408
+    # Diagonal tiles take 36 of 64 blocks in every form (the operand tile
+    # of the folded and direct forms is read in the diagonal tile too).
+    assert bench.executed_mfma_flops(1408, 2048, 1, "direct")["ns_poly"] == pytest.approx(
+        (10 * full + 5 * 36 / 64 * full + 3 * wide) * 1408)
+
+
+def test_f32_executed_flops_model():
+    # One 64 x 64 tile: Gram, Poly and Update each execute the nominal
+    # 2 m^2 n, 2 m^3 and 2 m^2 n.
+    assert bench.f32_executed_flops(64, 64, 5) == bench.nominal_ns_flops(64, 64, 5)
+    # 100 x 300 pads to 128 x 320: 3 upper tiles of 64 x 64 for Gram and Poly.
+    assert bench.f32_executed_flops(100, 300, 1) == 2 * 3 * 4096 * 320 + 2 * 3 * 4096 * 128 + 2 * 128 * 128 * 320
