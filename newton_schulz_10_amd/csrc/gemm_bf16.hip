@@ -49,14 +49,14 @@
 //    every 4 MFMAs): issued in a burst they back up the address unit and
 //    stall the wave's MFMA issue behind them.
 //  * Epilogues through LDS. Drain form (Update in the non-final steps, and
-//    the off-diagonal tiles of Gram and Poly, when no epilogue reads an
-//    operand tile):
+//    the full tiles of Gram and Poly, diagonal ones included, when no
+//    epilogue reads an operand tile):
 //    after one barrier in the last K-slab each wave forms its 128 x 128
 //    block in fp32 and passes it through a private 32 x 128 strip of the
 //    fourth stage to coalesced row stores (and transposing gathers for
 //    the mirror), with no further workgroup barrier; the next tile's
-//    prologue fills the other three stages meanwhile. Shared form
-//    (diagonal and wide tiles, operand tiles, the fused apply): the whole
+//    prologue fills the other three stages meanwhile. Shared form (wide
+//    tiles, operand tiles, the fused apply): the whole
 //    tile is formed in LDS (an operand tile loaded there first with
 //    coalesced direct loads) and leaves it as 16 B row stores and,
 //    transposed, as the mirror tile or the parameter's rows.
@@ -937,6 +937,8 @@ __device__ __forceinline__ void gemm_diag_tile(const GemmArgs& g, int mat, int I
   bf16_t* T = &lds[0][0];
   const bool dgon = g.diag_add != 0.0f;
   int claim = 0;
+  // Drain epilogue unless Poly reads its operand tile (see run).
+  const bool drain = !(ROLE == kPoly && g.poly_operand);
 
   // Main loop and fp32 epilogue of one wave kind. Same pipeline as the
   // general tile (fills three slabs ahead, one barrier per slab, fragments
@@ -1005,6 +1007,93 @@ __device__ __forceinline__ void gemm_diag_tile(const GemmArgs& g, int mat, int I
     slab(last - 1, std::integral_constant<int, 2>{}, std::false_type{});
     claim = claim_issue(cl, tid);
     slab(last, std::integral_constant<int, 3>{}, std::false_type{});
+
+    if (drain) {
+      // Drain epilogue (as in gemm_tile): after one barrier (every wave's
+      // last stage reads done) each wave takes its blocks through its own
+      // 32 x 128 strip of stage 3 (stage rows 0-255 are all a diagonal
+      // tile fills, so the claim slot at row 512 is free too), strip b =
+      // its row block b: the blocks on or below the diagonal of that row
+      // block (kind 0: a <= b, the diagonal block with its constant; kind
+      // 1: both) are formed, written, read back and stored as row runs;
+      // those strictly below the diagonal (kind 0: a < b; kind 1: both)
+      // are also gathered by columns and stored as the transposed blocks
+      // above the diagonal. A diagonal 32 x 32 block is exactly symmetric
+      // as computed and is stored once.
+      __builtin_amdgcn_s_waitcnt(vmcnt_lgkm0(63));
+      lds_barrier();
+      int etid = threadIdx.x;
+      asm volatile("" : "+v"(etid));
+      const int el = etid & 63, l32 = el & 31, hf = el >> 5;
+      const int rr = el >> 4, cc = el & 15, grp = el >> 4, jj = el & 15;
+      const int dsel = (KIND == 0 && hf == ((l32 >> 2) & 1)) ? 4 * (l32 >> 3) + (l32 & 3) : -1;
+      bf16_t* const W = &lds[kStages - 1][0] + wave * (32 * 128);
+      const int ld = g.m_pad;
+      bf16_t* const obase = static_cast<bf16_t*>(g.out) + (size_t)mat * g.mat_a;
+      bf16_t* const ob = obase + (size_t)(I * TILE + rbase) * ld + I * TILE + cbase;
+      bf16_t* const ob2 = obase + (size_t)(I * TILE + cbase) * ld + I * TILE + rbase;
+      const float scl = (ROLE == kPoly) ? g.cc : sc;
+#pragma unroll
+      for (int b = 0; b < 4; ++b) {
+        const int na = KIND == 0 ? b + 1 : 2;   // blocks of this row block
+        const int nm = KIND == 0 ? b : 2;       // of which below the diagonal
+#pragma unroll
+        for (int a = 0; a < na; ++a) {
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            float v[4];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              v[e] = acc[a][b][4 * q + e] * scl;
+              if (KIND == 0 && a == b && dgon) v[e] += (4 * q + e == dsel) ? g.diag_add : 0.0f;
+            }
+            uint2 o;
+            o.x = f32x2_to_bf16x2(v[0], v[1]);
+            o.y = f32x2_to_bf16x2(v[2], v[3]);
+            *reinterpret_cast<uint2*>(W + l32 * 128 + (((4 * a + q) ^ dswz(l32)) << 3) + 4 * hf) = o;
+          }
+        }
+        asm volatile("" ::: "memory");
+        uint4 v[8];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+          const int row = 4 * u + rr;
+          v[u] = *reinterpret_cast<const uint4*>(W + row * 128 + ((cc ^ dswz(row)) << 3));
+        }
+        keep_batch(v);
+        if (cc < 4 * na) {
+#pragma unroll
+          for (int u = 0; u < 8; ++u) store16_at(ob, (32 * b + 4 * u + rr) * ld + 8 * cc, v[u]);
+        }
+        if (nm > 0) {
+#pragma unroll
+          for (int u = 0; u < 2 * nm; ++u) {
+            const int c0 = 16 * u;
+            s16x4 h[2];
+#pragma unroll
+            for (int half = 0; half < 2; ++half) {
+              const int row = 8 * grp + 4 * half + (jj >> 2);
+              const int col = c0 + 4 * (jj & 3);
+              h[half] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                  (lds_s16x4*)(W + row * 128 + ((((col >> 3) ^ dswz(row)) << 3) | (col & 7))));
+            }
+            v[u] = __builtin_bit_cast(uint4, __builtin_shufflevector(h[0], h[1], 0, 1, 2, 3, 4, 5, 6, 7));
+          }
+          keep_batch(v);
+#pragma unroll
+          for (int u = 0; u < 2 * nm; ++u) store16_at(ob2, (16 * u + jj) * ld + 32 * b + 8 * grp, v[u]);
+        }
+        asm volatile("" ::: "memory");
+        if (ROLE == kGram && b == 1 && cl.ctr) {
+          int* const slot = reinterpret_cast<int*>(&lds[kStages - 1][512 * BK]);
+          if (etid == 0) *slot = claim_tile(cl, claim);
+          __builtin_amdgcn_s_waitcnt(vmcnt_lgkm0(63));
+          lds_barrier();
+          next = *slot;
+        }
+      }
+      return;
+    }
 
     __builtin_amdgcn_s_waitcnt(0x0070);  // vmcnt(0) lgkmcnt(0): stages no longer read
     lds_barrier();
@@ -1082,6 +1171,7 @@ __device__ __forceinline__ void gemm_diag_tile(const GemmArgs& g, int mat, int I
   } else {
     run(std::integral_constant<int, 1>{}, 128, wave == 1 ? 0 : 64);
   }
+  if (drain) return;
   claim_publish(cl, tid, claim);
   __syncthreads();
   next = claim_load(cl);
@@ -1254,9 +1344,9 @@ void ns_gemm_bf16(GemmArgs g) {
       }
       if (I == J) gemm_diag_tile<ROLE>(g, mat, I, lds, cl, next);
       else gemm_tile<ROLE, false>(g, mat, I, J, lds, cl, next);
-      // A drained tile (see gemm_tile) needs no barrier before the next
-      // fills.
-      if (I == J || (ROLE == kPoly && g.poly_operand)) __syncthreads();
+      // A drained tile (see gemm_tile, gemm_diag_tile) needs no barrier
+      // before the next fills.
+      if (ROLE == kPoly && g.poly_operand) __syncthreads();
     } else {
       gemm_tile<ROLE, true>(g, mat, G.F, 2 * (u - G.full), lds, cl, next);
       __syncthreads();   // the epilogue's LDS reads are done before the next fills
