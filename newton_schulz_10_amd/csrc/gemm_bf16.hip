@@ -48,15 +48,15 @@
 //  * The fill loads are interleaved with the MFMAs (one 1 KiB load after
 //    every 4 MFMAs): issued in a burst they back up the address unit and
 //    stall the wave's MFMA issue behind them.
-//  * Epilogues through LDS. Drain form (Update in the non-final steps, and
-//    the full tiles of Gram and Poly, diagonal ones included, when no
-//    epilogue reads an operand tile):
+//  * Epilogues through LDS. Drain form (Update, the fused apply of its
+//    last step included, and the full tiles of Gram and Poly, diagonal
+//    ones included, when no epilogue reads an operand tile):
 //    after one barrier in the last K-slab each wave forms its 128 x 128
 //    block in fp32 and passes it through a private 32 x 128 strip of the
 //    fourth stage to coalesced row stores (and transposing gathers for
 //    the mirror), with no further workgroup barrier; the next tile's
 //    prologue fills the other three stages meanwhile. Shared form (wide
-//    tiles, operand tiles, the fused apply): the whole
+//    Gram/Poly tiles, operand tiles): the whole
 //    tile is formed in LDS (an operand tile loaded there first with
 //    coalesced direct loads) and leaves it as 16 B row stores and,
 //    transposed, as the mirror tile or the parameter's rows.
@@ -281,7 +281,7 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& g, int mat, int I, int
   // tile. (An operand tile loaded strip by strip in the drain leaves its
   // load latency exposed on every strip: measured far slower than loading
   // it whole into the shared epilogue tile.)
-  const bool drain = (ROLE == kUpdate) ? (!g.ptab && !g.update_operand)
+  const bool drain = (ROLE == kUpdate) ? !g.update_operand
                                        : (!WIDE && I != J && !(ROLE == kPoly && g.poly_operand));
 
   // LDS fill of one K-slab in loads of 16 stage rows of 64 B (1 KiB); the
@@ -478,7 +478,12 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& g, int mat, int I, int
     // (Gram), thread 0 puts the claimed tile in stage 3 past the strips
     // (row 512 on: no full tile's fill reaches it, and stage 3 is next
     // filled after the next tile's first barrier) after the second strip,
-    // and every thread reads it after a barrier there. A wave's LDS
+    // and every thread reads it after a barrier there. With the fused
+    // apply (Update's last step) X' is not stored: each 16 B of O read back
+    // from the strip meets the parameter's matching 16 B, p' = alpha p -
+    // gamma O (or out = O), along rows for a wide member and through the
+    // transposing gathers for a tall one, with the arithmetic and bounds
+    // of the shared epilogue's apply. A wave's LDS
     // accesses complete in issue order, so no wait
     // separates a strip's writes from its reads or from the next strip's
     // writes. (Measured on Update: one strip at a time is faster than
@@ -501,8 +506,29 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& g, int mat, int I, int
       const float sv = g.scales[mat];
       sc = (ROLE == kGram) ? sv * sv : sv;
     }
-    auto run_drain = [&](auto scaled) {
+    // Fused apply (Update's last step).
+    ApplyEntry ent{nullptr, 0, 0};
+    float gam = 0.0f;
+    if (ROLE == kUpdate && g.ptab) {
+      ent = g.ptab[mat];
+      gam = g.gamma[ent.tr];
+    }
+    const bool upd = g.apply_mode == 0;
+    auto apply8 = [&](uint4 o, uint4 pv) {
+      if (!upd) return o;
+      const unsigned ow[4] = {o.x, o.y, o.z, o.w}, pw[4] = {pv.x, pv.y, pv.z, pv.w};
+      unsigned r[4];
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        const float r0 = fmaf(-gam, bf16_to_f32(ow[k] & 0xffffu), g.alpha * bf16_to_f32(pw[k] & 0xffffu));
+        const float r1 = fmaf(-gam, bf16_to_f32(ow[k] >> 16), g.alpha * bf16_to_f32(pw[k] >> 16));
+        r[k] = f32x2_to_bf16x2(r0, r1);
+      }
+      return uint4{r[0], r[1], r[2], r[3]};
+    };
+    auto run_drain = [&](auto scaled, auto apply) {
       constexpr bool SC = decltype(scaled)::value;
+      constexpr bool AP = decltype(apply)::value && ROLE == kUpdate;
 #pragma unroll
       for (int b = 0; b < 4; ++b) {
 #pragma unroll
@@ -520,6 +546,50 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& g, int mat, int I, int
         }
         asm volatile("" ::: "memory");
         uint4 v[kBatch];
+        if constexpr (AP) {
+          bf16_t* const dst = static_cast<bf16_t*>(ent.dst);
+          const size_t lp = (size_t)ent.ld;   // row stride of p as stored
+          uint4 pv[kBatch];
+          size_t off[kBatch];
+          bool ok[kBatch];
+          if (!ent.tr) {
+            // Wide member: strip rows are rows of p.
+#pragma unroll
+            for (int u = 0; u < kBatch; ++u) {
+              const int row = 4 * u + rr;
+              v[u] = *reinterpret_cast<const uint4*>(W + row * 128 + ((cc ^ dswz(row)) << 3));
+              const int gi = I * TILE + rb0 + 32 * b + row, gj = q0 + cb0 + 8 * cc;
+              ok[u] = live && gi < g.m && gj < g.n;
+              off[u] = ok[u] ? gi * lp + gj : 0;
+              pv[u] = upd ? *reinterpret_cast<const uint4*>(dst + off[u]) : uint4{0u, 0u, 0u, 0u};
+            }
+          } else {
+            // Tall member: p is n x m, wide element (i, j) is p[j][i]; a
+            // transposing gather gives 8 consecutive wide rows of a column.
+#pragma unroll
+            for (int u = 0; u < kBatch; ++u) {
+              const int c0 = 16 * u;
+              s16x4 h[2];
+#pragma unroll
+              for (int half = 0; half < 2; ++half) {
+                const int row = 8 * grp + 4 * half + (jj >> 2);
+                const int col = c0 + 4 * (jj & 3);
+                h[half] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                    (lds_s16x4*)(W + row * 128 + ((((col >> 3) ^ dswz(row)) << 3) | (col & 7))));
+              }
+              v[u] = __builtin_bit_cast(uint4, __builtin_shufflevector(h[0], h[1], 0, 1, 2, 3, 4, 5, 6, 7));
+              const int gj = q0 + cb0 + c0 + jj, gi = I * TILE + rb0 + 32 * b + 8 * grp;
+              ok[u] = live && gj < g.n && gi < g.m;
+              off[u] = ok[u] ? gj * lp + gi : 0;
+              pv[u] = upd ? *reinterpret_cast<const uint4*>(dst + off[u]) : uint4{0u, 0u, 0u, 0u};
+            }
+          }
+          keep_batch(v);
+          keep_batch(pv);
+#pragma unroll
+          for (int u = 0; u < kBatch; ++u)
+            if (ok[u]) *reinterpret_cast<uint4*>(dst + off[u]) = apply8(v[u], pv[u]);
+        } else {
 #pragma unroll
         for (int u = 0; u < kBatch; ++u) {
           const int row = 4 * u + rr;
@@ -529,6 +599,7 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& g, int mat, int I, int
         if (live) {
 #pragma unroll
           for (int u = 0; u < kBatch; ++u) store16_at(ob, (32 * b + 4 * u + rr) * ld + 8 * cc, v[u]);
+        }
         }
         if constexpr (kSym) {
           // Transposing gather: lane (grp, jj) receives column c0 + jj of
@@ -561,8 +632,15 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& g, int mat, int I, int
         }
       }
     };
-    if (ROLE == kPoly || g.scales) run_drain(std::true_type{});
-    else run_drain(std::false_type{});
+    using T1 = std::true_type;
+    using F0 = std::false_type;
+    if (ROLE == kUpdate && g.ptab) {
+      if (g.scales) run_drain(T1{}, T1{}); else run_drain(F0{}, T1{});
+    } else if (ROLE == kPoly || g.scales) {
+      run_drain(T1{}, F0{});
+    } else {
+      run_drain(F0{}, F0{});
+    }
     return;
   }
 
@@ -1310,7 +1388,7 @@ void ns_gemm_bf16(GemmArgs g) {
       else gemm_tile<ROLE, false>(g, mat, I, J, lds, cl, next);
       // After a drain epilogue the next prologue needs no barrier (it
       // fills stages 0-2; the drain used stage 3).
-      if (g.ptab || g.update_operand) __syncthreads();   // the epilogue's LDS reads are done before the next fills
+      if (g.update_operand) __syncthreads();   // the epilogue's LDS reads are done before the next fills
       t = sched ? __builtin_amdgcn_readfirstlane(next) : t + step;
     } else {
     if (u < G.full) {
