@@ -49,14 +49,14 @@
 //    every 4 MFMAs): issued in a burst they back up the address unit and
 //    stall the wave's MFMA issue behind them.
 //  * Epilogues through LDS. Drain form (Update, the fused apply of its
-//    last step included, and the full tiles of Gram and Poly, diagonal
-//    ones included, when no epilogue reads an operand tile):
+//    last step included, and every tile of Gram and Poly, diagonal and
+//    wide ones included, when no epilogue reads an operand tile):
 //    after one barrier in the last K-slab each wave forms its 128 x 128
 //    block in fp32 and passes it through a private 32 x 128 strip of the
 //    fourth stage to coalesced row stores (and transposing gathers for
 //    the mirror), with no further workgroup barrier; the next tile's
-//    prologue fills the other three stages meanwhile. Shared form (wide
-//    Gram/Poly tiles, operand tiles): the whole
+//    prologue fills the other three stages meanwhile. Shared form (tiles
+//    whose epilogue reads an operand tile): the whole
 //    tile is formed in LDS (an operand tile loaded there first with
 //    coalesced direct loads) and leaves it as 16 B row stores and,
 //    transposed, as the mirror tile or the parameter's rows.
@@ -281,8 +281,7 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& g, int mat, int I, int
   // tile. (An operand tile loaded strip by strip in the drain leaves its
   // load latency exposed on every strip: measured far slower than loading
   // it whole into the shared epilogue tile.)
-  const bool drain = (ROLE == kUpdate) ? !g.update_operand
-                                       : (!WIDE && I != J && !(ROLE == kPoly && g.poly_operand));
+  const bool drain = (ROLE == kUpdate) ? !g.update_operand : !(ROLE == kPoly && g.poly_operand);
 
   // LDS fill of one K-slab in loads of 16 stage rows of 64 B (1 KiB); the
   // loads are dealt round-robin over the waves (wave w issues loads w,
@@ -498,9 +497,14 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& g, int mat, int I, int
     bf16_t* const obase = static_cast<bf16_t*>(g.out) + (size_t)mat * ((ROLE == kUpdate) ? g.mat_x : g.mat_a);
     bf16_t* const ob = obase + (size_t)(I * TILE + rb0) * ld + q0 + cb0;
     bf16_t* const ob2 = obase + (size_t)(q0 + cb0) * ld + I * TILE + rb0;   // mirror (Gram/Poly)
-    // Wide Update tiles: a wave's 128 columns are all inside the padded
-    // width or all past it (both are multiples of 256 from q0).
+    // Wide tiles: a wave's 128 columns are all inside the padded width or
+    // all past it (both are multiples of 128 from q0). A wide Gram/Poly
+    // tile's wave whose block is on the diagonal stores it once (it is
+    // exactly symmetric as computed) with the diagonal constant.
     const bool live = !WIDE || cb0 < colmax - q0;
+    const bool dwave = kSym && WIDE && q0 + cb0 == I * TILE;
+    const int dsel = (dwave && hf == ((l32 >> 2) & 1)) ? 4 * (l32 >> 3) + (l32 & 3) : -1;
+    const bool dadd = dwave && g.diag_add != 0.0f;
     float sc = (ROLE == kPoly) ? g.cc : 1.0f;
     if (ROLE != kPoly && g.scales) {
       const float sv = g.scales[mat];
@@ -537,7 +541,10 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& g, int mat, int I, int
           for (int q = 0; q < 4; ++q) {
             float v[4];
 #pragma unroll
-            for (int e = 0; e < 4; ++e) v[e] = SC ? acc[a][b][4 * q + e] * sc : acc[a][b][4 * q + e];
+            for (int e = 0; e < 4; ++e) {
+              const float d = (kSym && WIDE && a == b && dadd && 4 * q + e == dsel) ? g.diag_add : -0.0f;
+              v[e] = SC ? fmaf(acc[a][b][4 * q + e], sc, d) : acc[a][b][4 * q + e] + d;
+            }
             uint2 o;
             o.x = f32x2_to_bf16x2(v[0], v[1]);
             o.y = f32x2_to_bf16x2(v[2], v[3]);
@@ -601,7 +608,7 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& g, int mat, int I, int
           for (int u = 0; u < kBatch; ++u) store16_at(ob, (32 * b + 4 * u + rr) * ld + 8 * cc, v[u]);
         }
         }
-        if constexpr (kSym) {
+        if (kSym && live && !dwave) {
           // Transposing gather: lane (grp, jj) receives column c0 + jj of
           // strip rows 8 grp .. +7 (two ds_read_b64_tr_b16 of 4 rows each),
           // 16 B of mirror row c0 + jj.
@@ -754,16 +761,17 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& g, int mat, int I, int
 #pragma unroll
             for (int e = 0; e < 4; ++e) v[e] = SC ? sc * fmaf(g.ca, x[e], v[e]) : fmaf(g.ca, x[e], v[e]);
           }
-        } else if (ROLE == kPoly) {
-#pragma unroll
-          for (int e = 0; e < 4; ++e) v[e] *= g.cc;
-        } else if (SC) {
-#pragma unroll
-          for (int e = 0; e < 4; ++e) v[e] *= sc;
         }
-        if (DG && a == b) {
+        // The diagonal constant joins the scaled product in one fmaf (one
+        // rounding, and no choice left to floating-point contraction);
+        // -0.0 leaves every other element exactly the plain product.
 #pragma unroll
-          for (int e = 0; e < 4; ++e) v[e] += (4 * q + e == dsel) ? g.diag_add : 0.0f;
+        for (int e = 0; e < 4; ++e) {
+          const float d = (DG && a == b && 4 * q + e == dsel) ? g.diag_add : -0.0f;
+          if (OP) v[e] = v[e] + d;
+          else if (ROLE == kPoly) v[e] = fmaf(v[e], g.cc, d);
+          else if (SC) v[e] = fmaf(v[e], sc, d);
+          else v[e] = v[e] + d;
         }
         uint2 o;
         o.x = f32x2_to_bf16x2(v[0], v[1]);
@@ -1122,8 +1130,8 @@ __device__ __forceinline__ void gemm_diag_tile(const GemmArgs& g, int mat, int I
             float v[4];
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
-              v[e] = acc[a][b][4 * q + e] * scl;
-              if (KIND == 0 && a == b && dgon) v[e] += (4 * q + e == dsel) ? g.diag_add : 0.0f;
+              const float d = (KIND == 0 && a == b && dgon && 4 * q + e == dsel) ? g.diag_add : -0.0f;
+              v[e] = fmaf(acc[a][b][4 * q + e], scl, d);
             }
             uint2 o;
             o.x = f32x2_to_bf16x2(v[0], v[1]);
@@ -1225,13 +1233,15 @@ __device__ __forceinline__ void gemm_diag_tile(const GemmArgs& g, int mat, int I
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
             v[e] = acc[a][b][4 * q + e];
+            // Diagonal constant in one fmaf with the scaled product (see
+            // gemm_tile); -0.0 elsewhere.
+            const float d = (KIND == 0 && a == b && dgon && 4 * q + e == dsel) ? g.diag_add : -0.0f;
             if (OP) {
               const unsigned h = (e < 2 ? w[q].x : w[q].y) >> (16 * (e & 1));
-              v[e] = fmaf(g.cb, bf16_to_f32(h & 0xffffu), g.cc * v[e]);
+              v[e] = fmaf(g.cb, bf16_to_f32(h & 0xffffu), g.cc * v[e]) + d;
             } else {
-              v[e] = (ROLE == kPoly) ? v[e] * g.cc : v[e] * sc;
+              v[e] = fmaf(v[e], (ROLE == kPoly) ? g.cc : sc, d);
             }
-            if (KIND == 0 && a == b && dgon) v[e] += (4 * q + e == dsel) ? g.diag_add : 0.0f;
           }
           uint2 o;
           o.x = f32x2_to_bf16x2(v[0], v[1]);
@@ -1427,7 +1437,7 @@ void ns_gemm_bf16(GemmArgs g) {
       if (ROLE == kPoly && g.poly_operand) __syncthreads();
     } else {
       gemm_tile<ROLE, true>(g, mat, G.F, 2 * (u - G.full), lds, cl, next);
-      __syncthreads();   // the epilogue's LDS reads are done before the next fills
+      if (ROLE == kPoly && g.poly_operand) __syncthreads();   // the epilogue's LDS reads are done before the next fills
     }
     // Dynamic schedule: the tile claimed during the epilogue (thread 0's
     // atomic, passed on through the workgroup's slot in global memory, as
