@@ -24,6 +24,25 @@ namespace {
 
 constexpr int T = kEwTile;  // 64
 
+// Workgroups of the momentum and apply passes resident on the chip at once:
+// 256 compute units x 8 (four waves each, one per SIMD, within the LDS and
+// register budget). A tall matrix with more tiles than this takes its tiles
+// along the stored rows (see tile_coords).
+constexpr int kEwResident = 256 * 8;
+
+// Wide tile (ti, tj) of workgroup index b. Wide matrices (and tall ones that
+// fit in the resident window) run the wide tile rows in order. A tall
+// matrix larger than the window runs the wide tile columns in order, so
+// consecutive workgroups read consecutive bands of the stored rows: in the
+// row-major wide order the resident workgroups would read 64-column strips
+// from every stored row at once, which measured 20-30% slower on MI355X for
+// 14336x4096 and 7168x2048; for 2048x1408 (704 tiles, all resident either
+// way) the wide order measured a few per cent faster.
+__device__ __forceinline__ void tile_coords(int b, int tiles_m, int tiles_n, bool tall, int& ti, int& tj) {
+  if (tall && tiles_m * tiles_n > kEwResident) { tj = b / tiles_m; ti = b % tiles_m; }
+  else { ti = b / tiles_n; tj = b % tiles_n; }
+}
+
 // The matrix table travels in the kernel argument block; keep it (with the
 // largest per-launch arguments) within 4 KiB.
 static_assert(sizeof(EwMats) + sizeof(MomentumArgs) <= 4096, "elementwise kernel arguments exceed 4 KiB");
@@ -110,7 +129,10 @@ __global__ __launch_bounds__(256) void momentum_kernel(EwMats mats, MomentumArgs
   __shared__ float red[4];
   const int mi = blockIdx.y;
   const int tiles_n = a.n_pad / T;
-  const int ti = blockIdx.x / tiles_n, tj = blockIdx.x % tiles_n;
+  // The tile's partial keeps its wide row-major index in either tile order.
+  int ti, tj;
+  tile_coords(blockIdx.x, a.m_pad / T, tiles_n, mats.tr[mi], ti, tj);
+  const int tile_id = ti * tiles_n + tj;
   const int tx = threadIdx.x & 15, ty = threadIdx.x >> 4;
   const GT* g = static_cast<const GT*>(mats.src[mi]);
   float* buf = mats.buf[mi];
@@ -241,8 +263,8 @@ __global__ __launch_bounds__(256) void momentum_kernel(EwMats mats, MomentumArgs
   const float tot = block_sum_256(ss, red);
   const int any = __syncthreads_or(nz);
   if (threadIdx.x == 0) {
-    a.partials[(size_t)(a.first + mi) * a.ew_blocks + blockIdx.x] = tot;
-    a.nonzero[(size_t)(a.first + mi) * a.ew_blocks + blockIdx.x] = any ? 1 : 0;
+    a.partials[(size_t)(a.first + mi) * a.ew_blocks + tile_id] = tot;
+    a.nonzero[(size_t)(a.first + mi) * a.ew_blocks + tile_id] = any ? 1 : 0;
   }
 }
 
@@ -268,12 +290,12 @@ template <typename PT, typename XT>
 __global__ __launch_bounds__(256) void apply_kernel(EwMats mats, ApplyArgs a) {
   __shared__ float tile[T][T + 1];
   const int mi = blockIdx.y;
-  const int tiles_n = (a.n_pad) / T;
-  const int ti = blockIdx.x / tiles_n, tj = blockIdx.x % tiles_n;
+  const int tr = mats.tr[mi];
+  int ti, tj;
+  tile_coords(blockIdx.x, (a.m + T - 1) / T, a.n_pad / T, tr, ti, tj);
   const int tx = threadIdx.x & 15, ty = threadIdx.x >> 4;
   const XT* x = static_cast<const XT*>(a.x) + (size_t)(a.first + mi) * a.mat_x;
   const float os = a.use_scale ? a.scales[a.first + mi] : 1.0f;
-  const int tr = mats.tr[mi];
   const float gamma = a.gamma[tr];
   // A matrix whose NS input was exactly zero has O = 0 exactly (its iterate
   // was not stored); with dead_only, live matrices are someone else's.
