@@ -324,6 +324,27 @@ def test_zero_matrices_with_weight_decay(nsa):
         assert np.array_equal(p1[i], want), i
 
 
+def test_large_tall_members_stored_row_order(nsa):
+    # Tall members with more 64x64 tiles than the workgroups resident on the
+    # chip (2048) take the momentum and apply passes' tiles along the stored
+    # rows. bf16: a live 4160 x 2048 member (2176 tiles) against the oracle,
+    # and an idle 8192 x 4096 member whose decay runs in the separate apply
+    # pass, checked exactly. float32: a live 4224 x 2112 member (2178 tiles),
+    # whose update runs in the separate apply pass.
+    case = workloads.random_case(31, [(4160, 2048), (8192, 4096)], "bf16", momentum_init="zero", zero=(1,))
+    p1, m1 = run_case(nsa, case, "bf16", 0.02, 0.95, 5, weight_decay=0.1)
+    ref = oracle_case(case[:1], 0.02, 0.95, 5, weight_decay=0.1)
+    assert_parity(case[:1], "bf16", p1[:1], m1[:1], ref, BF16_TOL)
+    alpha = np.float32(1.0 - float(np.float32(0.02)) * float(np.float32(0.1)))   # as the library forms it
+    p0 = case[1]["params"].as_f64().astype(np.float32)
+    assert np.array_equal(p1[1], workloads._store(p0 * alpha, "bf16").as_f64())
+    assert not np.any(m1[1])
+    case = workloads.random_case(32, [(4224, 2112)], "f32")
+    p1, m1 = run_case(nsa, case, "f32", 0.02, 0.95, 5)
+    ref = oracle_case(case, 0.02, 0.95, 5)
+    assert_parity(case, "f32", p1, m1, ref, F32_TOL)
+
+
 def test_non_default_stream(nsa):
     import torch
     case = workloads.random_case(12, [(256, 256)] * 2, "bf16")
