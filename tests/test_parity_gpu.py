@@ -345,6 +345,16 @@ def test_large_tall_members_stored_row_order(nsa):
     assert_parity(case, "f32", p1, m1, ref, F32_TOL)
 
 
+def test_maximum_dimension(nsa):
+    # One side at the largest accepted dimension (2^20): an 8 x 2^20 member
+    # (a Gram K loop of 32768 slabs, 2048 wide Update tiles) and its tall
+    # twin (32768 momentum tiles, taken along the stored rows).
+    case = workloads.random_case(33, [(8, 1 << 20), (1 << 20, 8)], "bf16", momentum_init="zero")
+    p1, m1 = run_case(nsa, case, "bf16", 0.02, 0.95, 5)
+    ref = oracle_case(case, 0.02, 0.95, 5)
+    assert_parity(case, "bf16", p1, m1, ref, BF16_TOL)
+
+
 def test_non_default_stream(nsa):
     import torch
     case = workloads.random_case(12, [(256, 256)] * 2, "bf16")
