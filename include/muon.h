@@ -108,7 +108,7 @@ enum {
  *     formed in fp32 from the A tile in Poly's epilogue and rounded once,
  *     X' = B' X with no operand tile: the a X term rides in B' as in the
  *     square form, but A's diagonal keeps its bits. The most accurate
- *     (0.78-0.95e-2); about 2% slower than the square form there.
+ *     (0.78-0.95e-2); about 1-2% slower than the square form there.
  * The float32 path always computes the direct form. */
 enum { MUON_POLY_DIRECT = 0, MUON_POLY_SQUARE = 1, MUON_POLY_FOLDED = 2 };
 
