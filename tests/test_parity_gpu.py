@@ -197,6 +197,30 @@ def test_orthogonalize_entry(nsa):
         assert np.array_equal(from_device(ins[2]), from_device(outs[2]))
 
 
+def test_orthogonalize_expert_shapes_and_zero(nsa):
+    # muon_orthogonalize at the expert-bank shape in both orientations (the
+    # output is written by the last Update's fused apply: along rows for the
+    # wide member, through transposing gathers for the tall one) with an
+    # all-zero member beside the tall one (skipped on the device, its output
+    # must be exactly zero), and a tall shape that takes the separate apply
+    # pass (300 x 130). Outputs start as NaN so every element is checked.
+    import torch
+    rng = np.random.default_rng(7)
+    for shape, zero in (((2048, 1408), True), ((1408, 2048), False), ((300, 130), False)):
+        st = [workloads._store(rng.standard_normal(shape).astype(np.float32) * 1e-3, "bf16")]
+        if zero:
+            st.append(workloads._store(np.zeros(shape, np.float32), "bf16"))
+        ins = [to_device(s, "bf16") for s in st]
+        outs = [torch.full_like(x, float("nan")) for x in ins]
+        nsa.muon_orthogonalize(ins, outs, 5)
+        torch.cuda.synchronize()
+        ref = oracle.newton_schulz(st[0].as_f64())
+        assert check_output(from_device(outs[0]), ref, "bf16", BF16_TOL, label=f"{shape}") <= BF16_TOL
+        if zero:
+            o = from_device(outs[1])
+            assert not np.any(np.isnan(o)) and not np.any(o)
+
+
 # ---- bitwise invariants of the batched design ------------------------------
 
 def _bits(ts):
