@@ -35,9 +35,9 @@ constexpr int kEwResident = 256 * 8;
 // matrix larger than the window runs the wide tile columns in order, so
 // consecutive workgroups read consecutive bands of the stored rows: in the
 // row-major wide order the resident workgroups would read 64-column strips
-// from every stored row at once, which measured 20-30% slower on MI355X for
-// 14336x4096 and 7168x2048; for 2048x1408 (704 tiles, all resident either
-// way) the wide order measured a few per cent faster.
+// from every stored row at once, which measured 27% slower on MI355X for
+// 14336x4096 and 3% slower for 7168x2048; for 2048x1408 (704 tiles, all
+// resident either way) the wide order measured 3.5% faster.
 __device__ __forceinline__ void tile_coords(int b, int tiles_m, int tiles_n, bool tall, int& ti, int& tj) {
   if (tall && tiles_m * tiles_n > kEwResident) { tj = b / tiles_m; ti = b % tiles_m; }
   else { ti = b / tiles_n; tj = b % tiles_n; }

@@ -16,8 +16,8 @@
 // of A' = A + beta I (about -1.17 against entries of A of about 1/m) and of
 // B' is rounded to bf16 after the constants are added, which loses most of
 // the bits of A's own diagonal; measured against the fp64 reference at
-// 1408 x 2048 the update's error is 1.0-1.25e-2 against 0.8-0.95e-2 for
-// the page's form. The direct form is the page's:
+// 1408 x 2048 (both orientations) the update's error is 1.23-1.25e-2
+// against 0.94-0.95e-2 for the page's form. The direct form is the page's:
 //   Gram   : A  = sc * X X^T
 //   Poly   : B  = b A + c (A A^T)        (the A tile read in the epilogue)
 //   Update : X' = sc * (a X + B X)       (the X tile read in the epilogue)

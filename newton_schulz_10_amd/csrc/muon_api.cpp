@@ -329,9 +329,9 @@ int run(const std::vector<MatRef>& mats, float lr, float beta, int ns_steps, muo
         g.nlive = nlive;
         // Dynamic tile schedule for Gram (its diagonal tiles multiply 36 of
         // 64 blocks, and K = n makes its tiles long); measured on the MoE
-        // bank it is 2.8% faster there and 0.6% / 1.3% slower for Poly and
-        // Update, whose tiles are shorter or all alike. The counters are
-        // zeroed by the compact kernel.
+        // bank it is 2.8% faster there, neutral for Poly and 6% slower for
+        // Update (all its tiles alike) at the default batch cap. The
+        // counters are zeroed by the compact kernel.
         g.sched = (skip_zero && r == 0) ? sched : nullptr;
         g.poly_operand = shifted ? 0 : 1;
         g.update_operand = (bf16 && !square && !folded) ? 1 : 0;
