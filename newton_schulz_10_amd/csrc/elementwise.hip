@@ -66,7 +66,7 @@ __device__ __forceinline__ void load4(const ST* p, int valid, float v[4]) {
 }
 
 // 4 whole elements at a 4-element-aligned address (interior tiles).
-// Aligned 4-element accesses of the interior tiles. Non-temporal: every
+// Non-temporal: every
 // byte of these passes is touched once (the workspace of a batch is far
 // larger than the L2), and streaming hints measured 4% faster for the
 // momentum pass.
