@@ -102,7 +102,7 @@ enum {
  *   MUON_POLY_DIRECT: the step as section 6.6 states it -- A = X X^T, B = b A
  *     + c A A (b A added in fp32 from the A tile in the epilogue), X' = a X +
  *     B X (a X added in fp32 from the X tile in the epilogue); A, B and X'
- *     are each rounded once. Error 0.86-1.26e-2; about 6% slower on the
+ *     are each rounded once. Error 0.86-1.26e-2; about 6-7% slower on the
  *     1408 x 2048 expert bank.
  *   MUON_POLY_FOLDED: A = X X^T exact (no shift), B' = a I + b A + c A A
  *     formed in fp32 from the A tile in Poly's epilogue and rounded once,
