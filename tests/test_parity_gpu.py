@@ -315,6 +315,24 @@ def test_group_step_entry_and_expert_bank(nsa):
     assert_parity(case, "bf16", [from_device(p) for p in P], [from_device(m) for m in M], ref, BF16_TOL)
 
 
+def test_a1b_tensor_is_one_matrix(nsa):
+    # An [A, 1, B] tensor is one A x B matrix of the (A, B) group (section
+    # 6.6, Figure 10(a)), not A matrices of 1 x B: its step is bitwise the
+    # A x B tensor's, and matches the oracle. Wide and tall.
+    import torch
+    case = workloads.random_case(12, [(192, 320), (320, 192)], "bf16")
+    P, G, M = upload_case(case, "bf16")
+    P3, G3, M3 = ([t.clone().unsqueeze(1) for t in ts] for ts in (P, G, M))
+    nsa.muon_step(list(zip(P, G, M)), 0.02, 0.95, 5)
+    nsa.muon_step(list(zip(P3, G3, M3)), 0.02, 0.95, 5)
+    torch.cuda.synchronize()
+    for i in range(2):
+        assert P3[i].shape == (P[i].shape[0], 1, P[i].shape[1])
+        assert torch.equal(P3[i].squeeze(1), P[i]) and torch.equal(M3[i].squeeze(1), M[i]), i
+    ref = oracle_case(case, 0.02, 0.95, 5)
+    assert_parity(case, "bf16", [from_device(p) for p in P], [from_device(m) for m in M], ref, BF16_TOL)
+
+
 def test_zero_and_nan_matrices(nsa):
     import torch
     case = workloads.random_case(11, [(128, 256)] * 3, "bf16", momentum_init="zero", zero=(1,))
