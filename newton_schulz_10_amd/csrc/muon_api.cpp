@@ -93,11 +93,20 @@ std::vector<hipEvent_t> g_free_events;
 std::map<std::string, ProfTotal> g_totals;
 std::vector<std::string> g_kind_order;
 
+// Events for the timing come from a free list (g_prof_mu held). A failed
+// event call clears HIP's last-error state, which the kernel launchers
+// read after each launch: profiling must never fail a step.
 hipEvent_t take_event() {
   if (!g_free_events.empty()) { hipEvent_t e = g_free_events.back(); g_free_events.pop_back(); return e; }
   hipEvent_t e = nullptr;
-  if (hipEventCreate(&e) != hipSuccess) return nullptr;
+  if (hipEventCreate(&e) != hipSuccess) {
+    (void)hipGetLastError();
+    return nullptr;
+  }
   return e;
+}
+void give_event(hipEvent_t e) {
+  if (e) g_free_events.push_back(e);
 }
 
 struct ProfScope {
@@ -109,13 +118,23 @@ struct ProfScope {
     if (!g_prof_on) return;
     p.kind = kind; p.flops = flops; p.bytes = bytes;
     p.e0 = take_event(); p.e1 = take_event();
-    if (!p.e0 || !p.e1) return;
-    on = hipEventRecord(p.e0, s) == hipSuccess;
+    on = p.e0 && p.e1 && hipEventRecord(p.e0, s) == hipSuccess;
+    if (!on) {
+      (void)hipGetLastError();
+      give_event(p.e0);
+      give_event(p.e1);
+    }
   }
   ~ProfScope() {
     if (!on) return;
     std::lock_guard<std::mutex> lk(g_prof_mu);
-    if (hipEventRecord(p.e1, s) == hipSuccess) g_pending.push_back(p);
+    if (hipEventRecord(p.e1, s) == hipSuccess) {
+      g_pending.push_back(p);
+    } else {
+      (void)hipGetLastError();
+      give_event(p.e0);
+      give_event(p.e1);
+    }
   }
 };
 
@@ -642,7 +661,11 @@ int muon_profile_read(muon_profile_entry* out, int cap, int reset) {
     float ms = 0.0f;
     hipError_t e = hipEventSynchronize(p.e1);
     if (e == hipSuccess) e = hipEventElapsedTime(&ms, p.e0, p.e1);
-    if (e != hipSuccess) { status = -MUON_ERR_HIP; g_err = hipGetErrorString(e); }
+    if (e != hipSuccess) {
+      (void)hipGetLastError();
+      status = -MUON_ERR_HIP;
+      g_err = hipGetErrorString(e);
+    }
     if (!g_totals.count(p.kind)) g_kind_order.push_back(p.kind);
     ProfTotal& t = g_totals[p.kind];
     t.launches += 1; t.ms += ms; t.flops += p.flops; t.bytes += p.bytes;
