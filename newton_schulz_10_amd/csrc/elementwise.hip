@@ -440,6 +440,11 @@ hipError_t launch_compact(const int* live, int count, int* live_list, int* nlive
 hipError_t launch_momentum(const EwMats& mats, const MomentumArgs& a, int src_bf16, int ws_bf16,
                            hipStream_t s) {
   if (a.count <= 0) return hipSuccess;
+  // The kernel reads its matrices from the table's kEwChunk slots and maps
+  // workgroups onto the padded shape's 64 x 64 tiles.
+  if (a.count > kEwChunk || a.m_pad % T || a.n_pad % T || a.m > a.m_pad || a.n > a.n_pad ||
+      a.ew_blocks != (a.m_pad / T) * (a.n_pad / T))
+    return hipErrorInvalidValue;
   dim3 grid(a.ew_blocks, a.count), block(256);
   if (src_bf16 && ws_bf16) hipLaunchKernelGGL((momentum_kernel<bf16_t, bf16_t>), grid, block, 0, s, mats, a);
   else if (!src_bf16 && ws_bf16) hipLaunchKernelGGL((momentum_kernel<float, bf16_t>), grid, block, 0, s, mats, a);
@@ -457,6 +462,7 @@ hipError_t launch_finalize(const FinalizeArgs& a, hipStream_t s) {
 hipError_t launch_apply(const EwMats& mats, const ApplyArgs& a, int p_bf16, int ws_bf16,
                         hipStream_t s) {
   if (a.count <= 0) return hipSuccess;
+  if (a.count > kEwChunk || a.n_pad % T || a.n > a.n_pad) return hipErrorInvalidValue;
   const int m_pad = (a.m + T - 1) / T * T;
   dim3 grid((m_pad / T) * (a.n_pad / T), a.count), block(256);
   if (p_bf16 && ws_bf16) hipLaunchKernelGGL((apply_kernel<bf16_t, bf16_t>), grid, block, 0, s, mats, a);
